@@ -1,0 +1,226 @@
+"""Seeded synthetic workloads for the paged KV append + paged attention step.
+
+This module is the only code shared by the HIP path's callers (tests,
+bench) and the oracle's callers.  It draws random things and sizes buffers;
+it holds none of the method's arithmetic (no slot computation, no
+attention, no softmax).
+
+What it produces, per workload:
+  * context lengths (after this step's append) and new-token counts per
+    sequence, decode sequences first, then prefill chunks;
+  * a block pool size and a block table per sequence, holding
+    ceil(ctx / 16) physical blocks drawn from a seeded permutation of the
+    pool (blocks scattered through the pool, as in a paged cache that
+    stores only real tokens -- danielfleming.xyz, "Static batching",
+    section "Ragged batches");
+  * per layer, N(0,1) fp16 K/V pools, queries and new K/V rows, drawn with a
+    seeded torch generator on the requested device.
+
+Sizing helpers restate the pages' capacity arithmetic (deepconcepts.dev,
+"Continuous Batching Is Not a Bigger Batch", section "Where the batch size
+actually comes from": bytes per token = 2 x layers x kv_heads x head_dim x
+bytes; blocks = tokens / 16 rounded up per sequence; pool blocks = whole
+16-token blocks that fit).
+
+Workload recipes (the five shapes the benchmark and parity tests use):
+  small_b4        1 layer, B=4, 12/2 heads, d=128, ctx {16,64,256,1024},
+                  128-block pool, tables = consecutive runs of a seeded
+                  permutation of the pool.
+  qwen_uniform    28 layers, B=256, ctx 512 each, 12/2 heads, d=128, pool
+                  ceil(1.2 x needed) blocks, tables from a seeded permutation.
+  qwen_ragged     28 layers, B=83, ctx = prompt + progress, prompt uniform on
+                  {16,64,256,1024,4096}, progress uniform on {0..256}.
+  long_context    16 layers, B=4, 16/4 heads, d=256, ctx 262,144 each, pool
+                  exactly the 65,536 blocks needed.
+  qwen_mixed      28 layers, 64 decode sequences with ctx uniform on
+                  [256, 4096] plus one prefill chunk of 512 query tokens on an
+                  8,192-token cached prefix (ctx 8,704).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_SIZE = 16
+FP16_BYTES = 2
+
+
+# ---------------------------------------------------------------- sizing ---
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_elem: float) -> float:
+    """K and V bytes one token occupies across all layers (2 x L x Hkv x d x bytes)."""
+    return 2 * layers * kv_heads * head_dim * bytes_per_elem
+
+
+def blocks_for_tokens(tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    """Whole blocks a sequence of `tokens` tokens holds."""
+    return -(-int(tokens) // block_size)
+
+
+def pool_blocks_for_bytes(pool_bytes: int, bytes_per_token: float, block_size: int = BLOCK_SIZE) -> int:
+    """Whole blocks that fit in a pool of `pool_bytes`."""
+    return int(pool_bytes // (bytes_per_token * block_size))
+
+
+# -------------------------------------------------------------- workload ---
+
+@dataclass
+class Workload:
+    name: str
+    num_layers: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    context_lens: np.ndarray          # int32 [B], includes this step's new tokens
+    new_tokens: np.ndarray            # int32 [B], 1 for decode sequences
+    num_decode_seqs: int
+    num_blocks: int                   # pool blocks per layer
+    block_tables: np.ndarray          # int32 [B, max_blocks_per_seq]
+    seed: int = 0
+    block_size: int = BLOCK_SIZE
+    free_blocks: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.context_lens.shape[0])
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.new_tokens.sum())
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def query_start_loc(self) -> np.ndarray:
+        """int32 [B+1]: row offset of each sequence's new tokens in the packed query."""
+        return np.concatenate([[0], np.cumsum(self.new_tokens)]).astype(np.int32)
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max())
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.new_tokens.max())
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    # byte model of one layer of the step (the quantities the method must move)
+    def kv_read_bytes_per_layer(self, decode_only: bool = False) -> int:
+        ctx = self.context_lens[: self.num_decode_seqs] if decode_only else self.context_lens
+        return int(ctx.astype(np.int64).sum()) * self.num_kv_heads * self.head_dim * 2 * FP16_BYTES
+
+    def qo_bytes_per_layer(self, decode_only: bool = False) -> int:
+        t = self.num_decode_seqs if decode_only else self.num_tokens
+        return 2 * t * self.num_q_heads * self.head_dim * FP16_BYTES
+
+    def append_bytes_per_layer(self) -> int:
+        return 2 * self.num_tokens * self.num_kv_heads * self.head_dim * FP16_BYTES
+
+
+def _tables_from_permutation(perm: np.ndarray, ctx: np.ndarray, block_size: int,
+                             fill_value: int) -> tuple[np.ndarray, np.ndarray]:
+    """Sequences take consecutive runs of `perm`, ceil(ctx/bs) blocks each."""
+    nb = np.array([blocks_for_tokens(c, block_size) for c in ctx], dtype=np.int64)
+    maxblk = int(nb.max()) if len(nb) else 1
+    tables = np.full((len(ctx), maxblk), fill_value, dtype=np.int32)
+    pos = 0
+    for i, n in enumerate(nb):
+        tables[i, :n] = perm[pos:pos + n]
+        pos += n
+    return tables, perm[pos:].astype(np.int32)
+
+
+def _build(name, layers, hq, hkv, d, ctx, new, n_dec, pool_factor, seed, pool_blocks=None):
+    rng = np.random.default_rng(seed)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    new = np.asarray(new, dtype=np.int32)
+    needed = int(sum(blocks_for_tokens(c) for c in ctx))
+    nblocks = pool_blocks if pool_blocks is not None else int(math.ceil(pool_factor * needed))
+    perm = rng.permutation(nblocks).astype(np.int32)
+    tables, free = _tables_from_permutation(perm, ctx, BLOCK_SIZE, fill_value=0)
+    return Workload(name=name, num_layers=layers, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                    context_lens=ctx, new_tokens=new, num_decode_seqs=n_dec, num_blocks=nblocks,
+                    block_tables=tables, seed=seed, free_blocks=free)
+
+
+def small_b4(seed: int = 0) -> Workload:
+    ctx = [16, 64, 256, 1024]
+    return _build("small_b4", 1, 12, 2, 128, ctx, [1] * 4, 4, None, seed, pool_blocks=128)
+
+
+def qwen_uniform(seed: int = 0, batch: int = 256, ctx_len: int = 512, layers: int = 28) -> Workload:
+    return _build("qwen_uniform", layers, 12, 2, 128, [ctx_len] * batch, [1] * batch, batch, 1.2, seed)
+
+
+def qwen_ragged(seed: int = 0, batch: int = 83, layers: int = 28) -> Workload:
+    rng = np.random.default_rng(seed + 1)
+    prompts = rng.choice(np.array([16, 64, 256, 1024, 4096]), size=batch)
+    progress = rng.integers(0, 256, size=batch, endpoint=True)
+    ctx = (prompts + progress).astype(np.int32)
+    return _build("qwen_ragged", layers, 12, 2, 128, ctx, [1] * batch, batch, 1.2, seed)
+
+
+def long_context(seed: int = 0, batch: int = 4, ctx_len: int = 262144, layers: int = 16) -> Workload:
+    needed = batch * blocks_for_tokens(ctx_len)
+    return _build("long_context", layers, 16, 4, 256, [ctx_len] * batch, [1] * batch, batch, None,
+                  seed, pool_blocks=needed)
+
+
+def qwen_mixed(seed: int = 0, decodes: int = 64, chunk: int = 512, prefix: int = 8192,
+               layers: int = 28) -> Workload:
+    rng = np.random.default_rng(seed + 2)
+    dec_ctx = rng.integers(256, 4096, size=decodes, endpoint=True)
+    ctx = np.concatenate([dec_ctx, [prefix + chunk]]).astype(np.int32)
+    new = np.array([1] * decodes + [chunk], dtype=np.int32)
+    return _build("qwen_mixed", layers, 12, 2, 128, ctx, new, decodes, 1.2, seed)
+
+
+def custom(name: str, ctx, new, num_decode_seqs: int, hq: int, hkv: int, d: int, layers: int = 1,
+           pool_factor: float = 1.5, seed: int = 0, pool_blocks: int | None = None) -> Workload:
+    """Arbitrary small shapes for parity and edge-case tests."""
+    return _build(name, layers, hq, hkv, d, ctx, new, num_decode_seqs, pool_factor, seed,
+                  pool_blocks=pool_blocks)
+
+
+WORKLOADS = {
+    "small_b4": small_b4,
+    "qwen_uniform": qwen_uniform,
+    "qwen_ragged": qwen_ragged,
+    "long_context": long_context,
+    "qwen_mixed": qwen_mixed,
+}
+
+
+# ------------------------------------------------------------------ data ---
+
+def layer_tensors(wl: Workload, layer: int, device="cpu"):
+    """N(0,1) fp16 tensors of one layer: k_pool, v_pool, q, k_new, v_new.
+
+    Drawn from a torch generator seeded by (seed, layer) on `device`, so a
+    layer can be regenerated on its own.
+    """
+    import torch
+
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed * 1_000_003 + layer * 7919 + 17)
+    shape_pool = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+    T = wl.num_tokens
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float16)
+
+    return {
+        "k_pool": randn(*shape_pool),
+        "v_pool": randn(*shape_pool),
+        "q": randn(T, wl.num_q_heads, wl.head_dim),
+        "k_new": randn(T, wl.num_kv_heads, wl.head_dim),
+        "v_new": randn(T, wl.num_kv_heads, wl.head_dim),
+    }
