@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark: one paged-attention step (all layers) on one MI355X.
+
+A step is one pass of the whole hot path over one batch: slot mapping once,
+then for every layer the KV append followed by paged attention (decode +
+split-KV merge, plus prefill chunks where the workload has them), all on one
+stream, inputs resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+value      = decode tokens per second of the whole step (decode sequences x
+             steps / wall time), wall time between synchronisations.
+roofline   = the dominant kernel (paged decode + its merge): algorithmic
+             bytes per launch (KV of every context, Q and O, block ids) over
+             the launch's average duration from HIP events around each
+             attention launch, against the 8 TB/s HBM peak.
+cpu_baseline = the fp64 CPU oracle, timed on the host on a bounded sample of
+             the same workload (a few layers of the step), scaled to a step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn step: KV-read HBM GB/s (% of peak) and decode tokens/s at 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "qwen_uniform"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--partition", type=int, default=0, help="force split-KV partition tokens")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes_per_attention_launch(wl) -> int:
+    """KV of every decode context + Q and O rows + block ids, one layer."""
+    ctx = wl.context_lens[: wl.num_decode_seqs].astype(np.int64)
+    kv = int(ctx.sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    qo = 2 * wl.num_decode_seqs * wl.num_q_heads * wl.head_dim * 2
+    ids = int((-(-ctx // wl.block_size)).sum()) * 4
+    return kv + qo + ids
+
+
+def cpu_baseline(wl, layer_tensors_dev, budget_s: float):
+    """Time the oracle (append replay + attention, fp64) on whole layers of
+    the step until the budget is spent; scale to decode tokens/s of a step."""
+    import torch
+    import oracle
+
+    qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, wl.block_size)
+    spent, layers = 0.0, 0
+    for t in layer_tensors_dev:
+        host = {k: v.detach().cpu().view(torch.int16).numpy().view(np.uint16) for k, v in t.items()}
+        t0 = time.perf_counter()
+        kp, vp = oracle.kv_append(host["k_pool"], host["v_pool"], host["k_new"], host["v_new"], slots)
+        oracle.paged_attention(host["q"], kp, vp, wl.block_tables, wl.context_lens, qsl, wl.scale)
+        spent += time.perf_counter() - t0
+        layers += 1
+        if spent >= budget_s:
+            break
+    per_step = spent / layers * wl.num_layers
+    return {
+        "value": wl.num_decode_seqs / per_step,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{layers} of {wl.num_layers} layers of one {wl.name} step "
+                  f"({spent:.1f} s), scaled to a whole step",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import paged_kv_decode_append_amd as pkv
+    from paged_kv_decode_append_amd.step import Step
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+
+    make = workloads.WORKLOADS[args.workload]
+    wl = make(layers=args.layers) if args.layers else make()
+    layers = [workloads.layer_tensors(wl, l, device="cuda") for l in range(wl.num_layers)]
+    caches = [pkv.KVCache(t["k_pool"], t["v_pool"]) for t in layers]
+    outs = [torch.empty_like(t["q"]) for t in layers]
+    step = Step.from_workload(wl, kv_partition_tokens=args.partition)
+    torch.cuda.synchronize()
+
+    def run_step():
+        step.plan()
+        for c, t, o in zip(caches, layers, outs):
+            step.layer(c, t["q"], t["k_new"], t["v_new"], o)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps between synchronisations.
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    # Per-launch duration of the attention (decode + merge) with HIP events
+    # on the launch stream, in a separate pass so events do not perturb the above.
+    stream = torch.cuda.current_stream()
+    n_ev = min(args.steps, 20) * wl.num_layers
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    k = 0
+    for _ in range(min(args.steps, 20)):
+        step.plan()
+        for c, t, o in zip(caches, layers, outs):
+            pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
+            ev[k][0].record(stream)
+            pkv.paged_attention_step(c, t["q"], o, step.block_tables, step.context_lens,
+                                     step.query_start_loc, step.num_decode_seqs, step.scale,
+                                     step.max_context_len, step.max_query_len,
+                                     workspace=step.workspace,
+                                     kv_partition_tokens=step.kv_partition_tokens)
+            ev[k][1].record(stream)
+            k += 1
+    torch.cuda.synchronize()
+    attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    alg_bytes = algorithmic_bytes_per_attention_launch(wl)
+    achieved = alg_bytes / (attn_us * 1e-6) / 1e9
+    kv_bytes_step = wl.kv_read_bytes_per_layer(decode_only=True) * wl.num_layers
+    result = {
+        "metric": METRIC,
+        "value": round(wl.num_decode_seqs / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "layers": wl.num_layers,
+            "batch": wl.num_seqs,
+            "decode_seqs": wl.num_decode_seqs,
+            "q_heads": wl.num_q_heads,
+            "kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim,
+            "block_size": wl.block_size,
+            "context_tokens": int(wl.context_lens.sum()),
+            "max_context": wl.max_context_len,
+            "pool_blocks_per_layer": wl.num_blocks,
+            "parallelism": "single-gpu",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "paged decode attention (+ split-KV merge when split)",
+            "alg_bytes_per_launch": alg_bytes,
+            "launch_us": round(attn_us, 2),
+        },
+        "kv_read_gbps_step": round(kv_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV append + paged attention step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  A continuous-batching engine re-forms its
+ * batch before every forward pass: each running sequence brings its
+ * num_new_tokens (one for a decoding sequence, a chunk of the prompt for a
+ * prefilling one) on top of num_computed_tokens, and the cache manager
+ * allocates cache slots for them before the pass runs (deepconcepts.dev,
+ * "Continuous Batching Is Not a Bigger Batch", section "What the scheduler
+ * does on one step").  The KV cache is held in fixed 16-token blocks
+ * (same page, section "The allocator is the other half"), so a sequence's
+ * cache is a list of physical blocks in logical order -- its block table --
+ * and a paged cache stores only real tokens (danielfleming.xyz, "Static
+ * batching", section "Ragged batches").  Every sequence carries one key and
+ * one value vector per token per layer ("Continuous Batching Is Not a Bigger
+ * Batch", introduction), with fewer KV heads than query heads (grouped-query
+ * attention, section "Where the batch size actually comes from").
+ *
+ * One step of one layer is:
+ *   1. pkv_slot_mapping  -- pool slot of every new token (shared by all layers);
+ *   2. pkv_kv_append     -- write each new token's K/V rows into its slot;
+ *   3. pkv_paged_attention_step -- every new query token attends its own
+ *      context through the block table: decode sequences (one token each)
+ *      over their whole context, prefill chunks causally.
+ *
+ * Conventions shared by every entry point.
+ *   - "device" pointers are GPU memory (hipMalloc / torch CUDA tensors),
+ *     "host" pointers are CPU memory.  The caller owns every buffer; the
+ *     library allocates nothing and keeps no per-call state.
+ *   - fp16 is IEEE binary16.  Integer arrays are little-endian, C order.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every GPU
+ *     entry point only enqueues work on `stream` and returns; it never
+ *     synchronises and never reads device memory from the host.
+ *   - Entry points validate their host-side scalars and pointers and return
+ *     a pkv_status; on any error nothing is enqueued.  They never abort and
+ *     never print.  Contents of device arrays (block ids, lengths, slots)
+ *     are a caller contract, checked only by pkv_validate_step; kernels
+ *     clamp block ids into the pool so that a broken contract gives wrong
+ *     numbers, not a memory fault.
+ *   - Context lengths include this step's new tokens: the append runs
+ *     first, then the attention reads the just-written tokens.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes      */
+  PKV_ERR_UNSUPPORTED = -2, /* block_size != 16, head_dim not 128/256, group > 8     */
+  PKV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required          */
+  PKV_ERR_HIP = -4,         /* a HIP launch or runtime call failed                 */
+  PKV_ERR_CONTRACT = -5     /* pkv_validate_step found a device-content violation  */
+} pkv_status;
+
+/*
+ * One layer's paged KV cache.  k_pool and v_pool are device fp16 arrays of
+ * shape [num_blocks][num_kv_heads][block_size][head_dim]: one block of one
+ * KV head is block_size * head_dim contiguous values (4 KiB at d = 128).
+ * Physical block b of KV head g holds the rows of block_size consecutive
+ * token positions of whichever sequence owns b.  Owned by the caller.
+ */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  int64_t num_blocks;
+  int32_t block_size;   /* must be 16 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t head_dim;     /* 128 or 256 */
+} pkv_kv_cache;
+
+/* Library version (PKV_VERSION of the build). */
+int pkv_version(void);
+
+/* Static string naming a pkv_status value ("PKV_OK", ...). */
+const char* pkv_status_string(int status);
+
+/*
+ * The HIP runtime error (hipError_t value) behind the most recent
+ * PKV_ERR_HIP returned on the calling thread, 0 if none; when `name` is not
+ * NULL it receives the runtime's static error string.  Host only.
+ */
+int pkv_last_hip_error(const char** name);
+
+/*
+ * Slot of every new token of the step (deepconcepts.dev, "Continuous
+ * Batching Is Not a Bigger Batch", "What the scheduler does on one step":
+ * new tokens sit on top of the computed ones, in blocks the cache manager
+ * allocated).  For sequence i with n_i new tokens and context length ctx_i,
+ * new token k is at logical position p = ctx_i - n_i + k and its slot is
+ *     block_tables[i][p / block_size] * block_size + p % block_size.
+ *
+ *   block_tables     device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens     device int32 [num_seqs], ctx_i >= n_i
+ *   query_start_loc  device int32 [num_seqs + 1], row of sequence i's first
+ *                    new token; n_i = qsl[i+1] - qsl[i].  NULL: every
+ *                    sequence has exactly one new token in row i.
+ *   slot_mapping     device int64 [num_tokens] (output); a position that
+ *                    falls outside its table row gets slot -1 (skipped by
+ *                    pkv_kv_append).
+ *   num_tokens       total new tokens (= qsl[num_seqs], or num_seqs when
+ *                    query_start_loc is NULL).
+ * Errors: PKV_ERR_INVALID_ARG (null pointer, negative size),
+ * PKV_ERR_UNSUPPORTED (block_size != 16), PKV_ERR_HIP.
+ */
+int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start_loc,
+                     int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                     int64_t* slot_mapping, void* stream);
+
+/*
+ * KV append: for every token t with slot_mapping[t] >= 0, copy the
+ * num_kv_heads x head_dim values of k_new[t] into
+ * k_pool[slot / block_size][g][slot % block_size][:] for every KV head g,
+ * and v_new[t] into v_pool likewise.  Bit-exact copy; slots < 0 are
+ * padding and are skipped; slots beyond the pool are skipped too (a broken
+ * contract, reported by pkv_validate_step).  Duplicate slots race.
+ *
+ *   cache         the layer's pools (device)
+ *   k_new, v_new  device fp16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  device int64 [num_tokens]
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+int pkv_kv_append(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+                  const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_step needs for a step of
+ * this shape (written to *bytes).  The same host-side hints must be passed
+ * to the step.  Pure host function: touches no GPU.
+ *
+ *   num_seqs, num_decode_seqs   sequences in the step; the first
+ *                               num_decode_seqs have one new token each
+ *   num_q_heads, num_kv_heads, head_dim
+ *   max_context_len             >= every ctx_i
+ *   max_query_len               >= every n_i (1 for a pure decode step)
+ *   kv_partition_tokens         0 = automatic; otherwise force this many
+ *                               context tokens per split-KV partition
+ *                               (multiple of 64)
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED.
+ */
+int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t max_query_len, int32_t kv_partition_tokens,
+                                 size_t* bytes);
+
+/*
+ * Paged attention over one layer for every new token of the step.
+ *
+ * Query row r of sequence i (row r = qsl[i] + k, k < n_i) sits at position
+ * pos = ctx_i - n_i + k and, for query head h, computes
+ *     out[r][h] = softmax_p( scale * q[r][h] . K_i[p][g] ) V_i[p][g],
+ *                 p = 0 .. pos,  g = h / (num_q_heads / num_kv_heads),
+ * where K_i[p] / V_i[p] are read from the pools through block_tables[i]
+ * (position p in table entry p / 16 at offset p % 16).  Decode sequences
+ * (the first num_decode_seqs, one token each) attend their whole context;
+ * the others are prefill chunks, attended causally.  Context positions at or
+ * beyond ctx_i, and table entries past ceil(ctx_i / 16), are never used,
+ * whatever they hold (NaN included).
+ *
+ *   cache            the layer's pools (device)
+ *   q                device fp16 [num_tokens][num_q_heads][head_dim]
+ *   out              device fp16 [num_tokens][num_q_heads][head_dim], written
+ *                    with round-to-nearest-even from fp32 accumulation
+ *   block_tables     device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens     device int32 [num_seqs]
+ *   query_start_loc  device int32 [num_seqs + 1], or NULL when every
+ *                    sequence is a decode sequence (row i = sequence i)
+ *   num_seqs, num_decode_seqs, num_q_heads, scale
+ *   max_context_len, max_query_len, kv_partition_tokens
+ *                    host hints, as for pkv_attention_workspace_size; the
+ *                    split-KV plan is made from these alone (no device read)
+ *   workspace        device buffer of at least the size that
+ *                    pkv_attention_workspace_size reports (may be NULL when
+ *                    that size is 0); contents need not be initialised and
+ *                    are undefined afterwards
+ * Launches: the decode kernel (grid over sequence x KV head x partition),
+ * the log-sum-exp merge of partitions when any sequence is split, and the
+ * MFMA prefill kernel when prefill chunks are present; all on `stream`.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
+ * PKV_ERR_HIP.
+ */
+int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t num_decode_seqs,
+                             int32_t num_q_heads, float scale,
+                             int32_t max_context_len, int32_t max_query_len,
+                             int32_t kv_partition_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Debug validator (host, synchronous, no GPU): checks on host copies of
+ * the step's index arrays every device-content contract the hot path
+ * assumes.  Returns PKV_OK, or PKV_ERR_CONTRACT with *bad_what set to one
+ * of the codes below and *bad_index to the first offending sequence (or
+ * token) index.  query_start_loc and slot_mapping may be NULL.
+ *   1  ctx_i < 1
+ *   2  ctx_i > max_blocks_per_seq * block_size
+ *   3  ctx_i < n_i, or query_start_loc not non-decreasing / inconsistent
+ *   4  a used block id (table entry < ceil(ctx_i / block_size)) outside
+ *      [0, num_blocks)
+ *   5  a decode sequence (i < num_decode_seqs) with n_i != 1
+ *   6  a slot outside [0, num_blocks * block_size) (negative = skipped)
+ *   7  two new tokens with the same non-negative slot
+ *   8  max_context_len or max_query_len smaller than an actual length
+ */
+int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* query_start_loc,
+                      int32_t num_seqs, int32_t num_decode_seqs, int64_t num_blocks,
+                      int32_t block_size, const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t max_context_len, int32_t max_query_len,
+                      int32_t* bad_what, int64_t* bad_index);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,202 @@
+// api.hip -- the extern "C" entry points of libpkv.so declared in include/pkv.h.
+//
+// Every entry point checks its host scalars and pointers first and returns
+// an error before touching the GPU, so argument errors are reported on a
+// machine without one.  Device arrays are never read from the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int32_t kBlockSize = 16;
+constexpr int32_t kMaxGroup = 8;
+constexpr int32_t kMaxGridYZ = 65535;
+
+bool supported_head_dim(int32_t d) { return d == 128 || d == 256; }
+
+int check_cache(const pkv_kv_cache* cache) {
+  if (!cache || !cache->k_pool || !cache->v_pool) return PKV_ERR_INVALID_ARG;
+  if (cache->num_blocks <= 0 || cache->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
+  if (cache->block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (!supported_head_dim(cache->head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (cache->num_kv_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+// Host-hint checks shared by the workspace query and the step.
+int check_step_shape(int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                     int32_t max_query_len, int32_t kv_partition_tokens) {
+  if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_q_heads / num_kv_heads > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (max_context_len < 1 || max_query_len < 1)) return PKV_ERR_INVALID_ARG;
+  if (kv_partition_tokens < 0 || kv_partition_tokens % 64 != 0 || kv_partition_tokens > 4096)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs > num_decode_seqs) return PKV_ERR_UNSUPPORTED;  // prefill chunks: not built yet
+  return PKV_OK;
+}
+
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return PKV_OK;
+  t_last_hip_error = e;
+  return PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return PKV_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_CONTRACT: return "PKV_ERR_CONTRACT";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+int pkv_last_hip_error(const char** name) {
+  if (name) *name = t_last_hip_error == hipSuccess ? "hipSuccess" : hipGetErrorName(t_last_hip_error);
+  return (int)t_last_hip_error;
+}
+
+int pkv_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start_loc,
+                     int32_t num_seqs, int32_t num_tokens, int32_t block_size,
+                     int64_t* slot_mapping, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!query_start_loc && num_tokens != num_seqs) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_slot_mapping(block_tables, max_blocks_per_seq, context_lens,
+                                           query_start_loc, num_seqs, num_tokens, slot_mapping,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int pkv_kv_append(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+                  const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  return from_hip(pkv::launch_kv_append(cache->k_pool, cache->v_pool, cache->num_blocks,
+                                        cache->num_kv_heads, cache->head_dim, k_new, v_new,
+                                        slot_mapping, num_tokens,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
+                                 int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t max_query_len, int32_t kv_partition_tokens,
+                                 size_t* bytes) {
+  if (!bytes) return PKV_ERR_INVALID_ARG;
+  int rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, num_kv_heads, head_dim,
+                            max_context_len, max_query_len, kv_partition_tokens);
+  if (rc != PKV_OK) return rc;
+  pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, num_kv_heads, num_q_heads, head_dim,
+                                          max_context_len, kv_partition_tokens);
+  if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  *bytes = plan.partial_bytes;
+  return PKV_OK;
+}
+
+int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t num_decode_seqs,
+                             int32_t num_q_heads, float scale,
+                             int32_t max_context_len, int32_t max_query_len,
+                             int32_t kv_partition_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_cache(cache);
+  if (rc != PKV_OK) return rc;
+  rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, cache->num_kv_heads,
+                        cache->head_dim, max_context_len, max_query_len, kv_partition_tokens);
+  if (rc != PKV_OK) return rc;
+  if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !out || !block_tables || !context_lens || max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
+    return PKV_ERR_INVALID_ARG;
+  (void)query_start_loc;
+  pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, cache->num_kv_heads, num_q_heads,
+                                          cache->head_dim, max_context_len, kv_partition_tokens);
+  if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  if (plan.partial_bytes > 0 && (!workspace || workspace_bytes < plan.partial_bytes))
+    return PKV_ERR_WORKSPACE;
+  return from_hip(pkv::launch_paged_decode(
+      q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
+      cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
+      plan, out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, const int32_t* query_start_loc,
+                      int32_t num_seqs, int32_t num_decode_seqs, int64_t num_blocks,
+                      int32_t block_size, const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t max_context_len, int32_t max_query_len,
+                      int32_t* bad_what, int64_t* bad_index) {
+  if (!bad_what || !bad_index) return PKV_ERR_INVALID_ARG;
+  *bad_what = 0;
+  *bad_index = -1;
+  if (num_seqs < 0 || num_decode_seqs < 0 || num_decode_seqs > num_seqs || num_tokens < 0 ||
+      max_blocks_per_seq <= 0 || num_blocks <= 0 || block_size <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_INVALID_ARG;
+  auto fail = [&](int32_t what, int64_t index) {
+    *bad_what = what;
+    *bad_index = index;
+    return (int)PKV_ERR_CONTRACT;
+  };
+  if (query_start_loc && query_start_loc[0] != 0) return fail(3, 0);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t ctx = context_lens[i];
+    const int32_t n = query_start_loc ? query_start_loc[i + 1] - query_start_loc[i] : 1;
+    if (ctx < 1) return fail(1, i);
+    if ((int64_t)ctx > (int64_t)max_blocks_per_seq * block_size) return fail(2, i);
+    if (n < 0 || ctx < n) return fail(3, i);
+    if (i < num_decode_seqs && n != 1) return fail(5, i);
+    if (ctx > max_context_len || n > max_query_len) return fail(8, i);
+    const int64_t used = ((int64_t)ctx + block_size - 1) / block_size;
+    for (int64_t j = 0; j < used; ++j) {
+      const int64_t b = block_tables[(int64_t)i * max_blocks_per_seq + j];
+      if (b < 0 || b >= num_blocks) return fail(4, i);
+    }
+  }
+  if (query_start_loc && query_start_loc[num_seqs] != num_tokens) return fail(3, num_seqs);
+  if (!query_start_loc && num_tokens != num_seqs) return fail(3, num_seqs);
+  if (slot_mapping) {
+    std::unordered_set<int64_t> seen;
+    seen.reserve((size_t)num_tokens * 2);
+    for (int32_t t = 0; t < num_tokens; ++t) {
+      const int64_t s = slot_mapping[t];
+      if (s < 0) continue;
+      if (s >= num_blocks * block_size) return fail(6, t);
+      if (!seen.insert(s).second) return fail(7, t);
+    }
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,487 @@
+// decode.hip -- paged decode attention with split-KV partitions, and the
+// log-sum-exp merge of partitions.
+//
+// Each decode sequence attends its one new query token over its whole
+// context, read through its block table (deepconcepts.dev, "Continuous
+// Batching Is Not a Bigger Batch": the batch is re-formed every pass and
+// its cache is allocated in fixed 16-token blocks; danielfleming.xyz,
+// "Static batching", section "Ragged batches": a paged layout stores only
+// real tokens, so a ragged mix does not pay for its widest member).
+//
+// Work decomposition (gfx950, wave64):
+//   grid = (sequence, KV head, partition); a work-group of 4 waves reads the
+//   partition's blocks of ONE KV head once and applies them to all G query
+//   heads of that group (grouped-query attention), so every K/V byte leaves
+//   HBM once per step.
+//   Blocks of the partition are dealt round-robin to the waves; each wave
+//   prefetches its next block into registers while it computes the current
+//   one, and fetches all its block ids with one vector load up front.
+//
+// Per block (16 tokens x d) and wave:
+//   K layout: D/16 lanes share one token row, each lane holding 16 of its
+//     d values (two 16-byte chunks), so a K load instruction reads whole
+//     128-byte runs of rows.  q.k is 8 packed fp16 dot products
+//     (v_dot2_f32_f16, fp32 accumulate) per head, then a DPP butterfly
+//     inside the lane group.
+//   Online softmax, base 2: scores are scaled by scale*log2(e); the running
+//     max m is wave-uniform and only raised when a score exceeds it by more
+//     than 8 (then the accumulators are rescaled), so weights p = 2^(s-m)
+//     stay in (0, 256] and the common case does no rescale.
+//   V layout: every lane owns d/64 output elements of all 16 tokens, so the
+//     P.V accumulation needs no cross-lane reduction.  The weights travel
+//     from the K layout to all lanes through a small per-wave LDS buffer as
+//     fp16 pairs of tokens (the two tokens a lane group scores in
+//     consecutive K steps), and P.V is again v_dot2_f32_f16 over those pairs.
+//   Masking is by select: positions >= ctx get score -inf and their V rows
+//   are zeroed before use, so stale or NaN-poisoned slots never leak.
+// At the end the 4 waves' (m, l, acc) merge through LDS; a sequence with a
+// single partition writes fp16 output directly, otherwise the partition
+// writes (o / l, m, l) and the merge kernel combines partitions:
+//   M = max_p m_p, w_p = l_p 2^(m_p - M), O = sum_p w_p o_p / sum_p w_p.
+#include <algorithm>
+#include <climits>
+
+#include "device_util.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kWaves = 4;                 // waves per work-group
+constexpr int kMaxBlocksPerWave = 64;     // one block id per lane
+constexpr int kMaxPartitionBlocks = kWaves * kMaxBlocksPerWave;
+constexpr int kTargetGroups = 512;        // work-groups that keep 256 CUs busy
+constexpr int kMinPartitionBlocks = 16;   // 256 tokens
+constexpr float kRescaleSlack = 8.f;      // lazy max: rescale only past m + 8 (base 2)
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D> struct VFrag;
+template <> struct VFrag<128> { typedef uint32_t T; };
+template <> struct VFrag<256> { typedef uint2 T; };
+
+template <int D>
+struct KVRegs {
+  static constexpr int LPT = D / 16;    // lanes sharing one K row
+  static constexpr int TPS = 64 / LPT;  // tokens covered by one wave-wide K load
+  static constexpr int SPB = 16 / TPS;  // K loads (steps) per 16-token block
+  uint4 k[SPB][2];
+  typename VFrag<D>::T v[16];
+};
+
+template <int D, int G>
+struct WaveState {
+  float m[G];           // running max of base-2 scores (wave-uniform)
+  float l[G];           // sum of weights over this lane group's tokens
+  float acc[G][D / 64]; // sum of weight * v over this lane's output elements
+};
+
+template <int D>
+__device__ __forceinline__ void load_kv(KVRegs<D>& r, const uint16_t* __restrict__ ktile,
+                                        const uint16_t* __restrict__ vtile, int lane) {
+  constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
+  const int tl = lane / LPT, c = lane % LPT;
+#pragma unroll
+  for (int s = 0; s < SPB; ++s)
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch)
+      r.k[s][ch] =
+          *reinterpret_cast<const uint4*>(ktile + (tl + TPS * s) * D + 8 * (c + LPT * ch));
+#pragma unroll
+  for (int t = 0; t < 16; ++t)
+    r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
+}
+
+__device__ __forceinline__ float dot16(const uint32_t (&q)[8], const uint4& a, const uint4& b) {
+  float s = 0.f;
+  s = dot2(q[0], a.x, s);
+  s = dot2(q[1], a.y, s);
+  s = dot2(q[2], a.z, s);
+  s = dot2(q[3], a.w, s);
+  s = dot2(q[4], b.x, s);
+  s = dot2(q[5], b.y, s);
+  s = dot2(q[6], b.z, s);
+  s = dot2(q[7], b.w, s);
+  return s;
+}
+
+// P.V over one token pair for one packed dword of V per token:
+// lo element pair (a.lo, b.lo), hi element pair (a.hi, b.hi).
+template <int G>
+__device__ __forceinline__ void pv_dword(float (&acc)[G][2], const uint32_t (&pr)[G], uint32_t a,
+                                         uint32_t b) {
+  const uint32_t lo = (a & 0xffffu) | (b << 16);
+  const uint32_t hi = (a >> 16) | (b & 0xffff0000u);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    acc[h][0] = dot2(pr[h], lo, acc[h][0]);
+    acc[h][1] = dot2(pr[h], hi, acc[h][1]);
+  }
+}
+
+// One 16-token block: scores, lazy-max online softmax, P.V.
+// tok0 = logical position of the block's first token.
+template <int D, int G>
+__device__ __forceinline__ void attend_block(KVRegs<D>& r, const uint32_t (&q)[G][8],
+                                             WaveState<D, G>& st, int tok0, int ctx,
+                                             float scale_log2, uint32_t* __restrict__ p_lds,
+                                             int lane) {
+  constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
+  constexpr int GP = (G + 3) & ~3;
+  const int tl = lane / LPT, c = lane % LPT;
+  const bool tail = tok0 + 16 > ctx;
+  const float kNegInf = -__builtin_huge_valf();
+
+  // Scores of this lane group's SPB tokens (tl + TPS*s) for every head.
+  float x[SPB][G];
+#pragma unroll
+  for (int s = 0; s < SPB; ++s)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      x[s][h] = group_sum<LPT>(dot16(q[h], r.k[s][0], r.k[s][1])) * scale_log2;
+  if (tail) {
+#pragma unroll
+    for (int s = 0; s < SPB; ++s) {
+      const bool valid = tok0 + tl + TPS * s < ctx;
+#pragma unroll
+      for (int h = 0; h < G; ++h) x[s][h] = valid ? x[s][h] : kNegInf;
+    }
+  }
+
+  // Raise the running max only when a score passes it by the slack.
+  bool grow = false;
+#pragma unroll
+  for (int s = 0; s < SPB; ++s)
+#pragma unroll
+    for (int h = 0; h < G; ++h) grow |= x[s][h] > st.m[h] + kRescaleSlack;
+  if (__any(grow)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float bm = x[0][h];
+#pragma unroll
+      for (int s = 1; s < SPB; ++s) bm = fmaxf(bm, x[s][h]);
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+      const float mn = fmaxf(st.m[h], bm);
+      const float alpha = fast_exp2(st.m[h] - mn);
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) st.acc[h][e] *= alpha;
+      st.m[h] = mn;
+    }
+  }
+
+  // Weights as fp16 pairs of tokens (tl + 2j*TPS, tl + (2j+1)*TPS); l sums
+  // exactly the rounded weights that P.V uses.
+  uint32_t pp[SPB / 2][G];
+#pragma unroll
+  for (int j = 0; j < SPB / 2; ++j)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pp[j][h] = pack_h2_rtz(fast_exp2(x[2 * j][h] - st.m[h]),
+                             fast_exp2(x[2 * j + 1][h] - st.m[h]));
+      st.l[h] = dot2(pp[j][h], kOnesH2, st.l[h]);
+    }
+  // Pair index pi = j*TPS + tl; one writer lane per group.
+  if (c == 0) {
+#pragma unroll
+    for (int j = 0; j < SPB / 2; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) p_lds[(j * TPS + tl) * GP + h] = pp[j][h];
+  }
+  wave_fence();
+
+  if (tail) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (tok0 + t >= ctx) r.v[t] = typename VFrag<D>::T{};
+  }
+
+  // P.V: pair pi holds tokens ta = pi%TPS + 2*TPS*(pi/TPS) and tb = ta + TPS.
+#pragma unroll
+  for (int pi = 0; pi < 8; ++pi) {
+    const int ta = pi % TPS + 2 * TPS * (pi / TPS), tb = ta + TPS;
+    uint32_t pr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
+    if constexpr (D == 128) {
+      pv_dword<G>(reinterpret_cast<float(&)[G][2]>(st.acc), pr, r.v[ta], r.v[tb]);
+    } else {
+      float lo[G][2], hi[G][2];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        lo[h][0] = st.acc[h][0]; lo[h][1] = st.acc[h][1];
+        hi[h][0] = st.acc[h][2]; hi[h][1] = st.acc[h][3];
+      }
+      pv_dword<G>(lo, pr, r.v[ta].x, r.v[tb].x);
+      pv_dword<G>(hi, pr, r.v[ta].y, r.v[tb].y);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        st.acc[h][0] = lo[h][0]; st.acc[h][1] = lo[h][1];
+        st.acc[h][2] = hi[h][0]; st.acc[h][3] = hi[h][1];
+      }
+    }
+  }
+  wave_fence();
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
+    int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int LPT = D / 16, EPL = D / 64, GP = (G + 3) & ~3;
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ uint32_t s_p[kWaves][8 * GP];
+
+  const int i = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
+  const int num_q_heads = num_kv_heads * G;
+  // A length beyond the table row or the planned partitions breaks the
+  // caller contract; clamp so that it can only give wrong numbers.
+  const int ctx = min(context_lens[i], ctx_clamp);
+  const int nblk = (ctx + 15) >> 4;
+  const int b0 = part * partition_blocks;
+  if (ctx <= 0 || b0 >= nblk) return;  // uniform over the work-group
+  const int b1 = min(b0 + partition_blocks, nblk);
+  const int nparts = (nblk + partition_blocks - 1) / partition_blocks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane % LPT;
+
+  // Block ids of this wave's blocks b0 + wave + kWaves*k, one per lane,
+  // clamped into the pool.
+  const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;
+  const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
+  int my_bid = 0;
+  if (lane < nbw) {
+    const uint32_t b = (uint32_t)bt_row[b0 + wave + kWaves * lane];
+    my_bid = (int)(b < (uint64_t)num_blocks ? b : (uint32_t)(num_blocks - 1));
+  }
+
+  // Query fragments of the G heads in the K layout.
+  uint32_t qf[G][8];
+  const uint16_t* qrow = q + ((int64_t)i * num_q_heads + (int64_t)g * G) * D;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 a = *reinterpret_cast<const uint4*>(qrow + h * D + 8 * c);
+    const uint4 b = *reinterpret_cast<const uint4*>(qrow + h * D + 8 * (c + LPT));
+    qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
+    qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
+  }
+
+  WaveState<D, G> st;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = -__builtin_huge_valf();
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[h][e] = 0.f;
+  }
+
+  const int64_t tile_elems = (int64_t)16 * D;
+  const int64_t head_off = (int64_t)g * tile_elems;
+  const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
+  if (nbw > 0) {
+    KVRegs<D> A, B;
+    int bid = __builtin_amdgcn_readlane(my_bid, 0);
+    load_kv<D>(A, k_pool + bid * block_stride + head_off, v_pool + bid * block_stride + head_off,
+               lane);
+    for (int k = 0; k < nbw; k += 2) {
+      if (k + 1 < nbw) {
+        bid = __builtin_amdgcn_readlane(my_bid, k + 1);
+        load_kv<D>(B, k_pool + bid * block_stride + head_off,
+                   v_pool + bid * block_stride + head_off, lane);
+      }
+      attend_block<D, G>(A, qf, st, (b0 + wave + kWaves * k) * 16, ctx, scale_log2, s_p[wave],
+                         lane);
+      if (k + 1 >= nbw) break;
+      if (k + 2 < nbw) {
+        bid = __builtin_amdgcn_readlane(my_bid, k + 2);
+        load_kv<D>(A, k_pool + bid * block_stride + head_off,
+                   v_pool + bid * block_stride + head_off, lane);
+      }
+      attend_block<D, G>(B, qf, st, (b0 + wave + kWaves * (k + 1)) * 16, ctx, scale_log2,
+                         s_p[wave], lane);
+    }
+  }
+
+  // Lane groups' weight sums -> wave totals.
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) st.l[h] += __shfl_xor(st.l[h], off);
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * lane + e] = st.acc[h][e];
+    if (lane == 0) {
+      s_m[wave][h] = st.m[h];
+      s_l[wave][h] = st.l[h];
+    }
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+    const int h = idx / D, e = idx - h * D;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (s_l[w][h] > 0.f) {
+        const float wt = fast_exp2(s_m[w][h] - M);
+        L += wt * s_l[w][h];
+        O += wt * s_acc[w][h][e];
+      }
+    }
+    const int64_t row_head = (int64_t)i * num_q_heads + g * G + h;
+    if (nparts == 1) {
+      out[row_head * D + e] = __builtin_bit_cast(uint16_t, (f16)(O / L));
+    } else {
+      const int64_t pidx = row_head * max_parts + part;
+      part_o[pidx * D + e] = O / L;
+      if (e == 0) {
+        part_ml[pidx * 2] = M;
+        part_ml[pidx * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// One wave per (sequence, query head) with more than one partition.
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
+    int32_t max_parts, int32_t num_q_heads, int32_t num_rows, uint16_t* __restrict__ out) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row_head = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row_head >= num_rows) return;
+  const int i = row_head / num_q_heads;
+  const int nblk = (min(context_lens[i], ctx_clamp) + 15) >> 4;
+  const int np = (nblk + partition_blocks - 1) / partition_blocks;
+  if (np <= 1) return;
+  const float* ml = part_ml + (int64_t)row_head * max_parts * 2;
+  const float* po = part_o + (int64_t)row_head * max_parts * D + EPL * lane;
+
+  float M = -__builtin_huge_valf();
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float W = 0.f, o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+    W += w;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] += w * po[(int64_t)p * D + e];
+  }
+  uint16_t* dst = out + (int64_t)row_head * D + EPL * lane;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = __builtin_bit_cast(uint16_t, (f16)(o[e] / W));
+}
+
+template <int D, int G>
+hipError_t launch_decode_dg(const void* q, const void* k_pool, const void* v_pool,
+                            int64_t num_blocks, int32_t num_kv_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_decode_seqs, float scale,
+                            const DecodePlan& plan, void* out, void* workspace,
+                            hipStream_t stream) {
+  const int32_t num_q_heads = num_kv_heads * G;
+  const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
+                                            (int64_t)plan.max_parts * plan.partition_blocks * 16);
+  const int32_t ctx_clamp = (int32_t)std::min<int64_t>(clamp64, INT32_MAX);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml =
+      part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  hipLaunchKernelGGL((paged_decode_kernel<D, G>),
+                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
+                     stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool),
+                     num_blocks, num_kv_heads, block_tables, max_blocks_per_seq, context_lens,
+                     ctx_clamp, plan.partition_blocks, plan.max_parts, scale * kLog2e,
+                     static_cast<uint16_t*>(out), part_o, part_ml);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_parts <= 1) return err;
+  const int32_t rows = num_decode_seqs * num_q_heads;
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  hipLaunchKernelGGL((lse_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream, part_o,
+                     part_ml, context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts,
+                     num_q_heads, rows, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(int32_t group, const void* q, const void* k_pool, const void* v_pool,
+                           int64_t num_blocks, int32_t num_kv_heads, const int32_t* bt,
+                           int32_t maxblk, const int32_t* ctx, int32_t nseq, float scale,
+                           const DecodePlan& plan, void* out, void* ws, hipStream_t stream) {
+#define PKV_CASE(GG)                                                                          \
+  case GG:                                                                                   \
+    return launch_decode_dg<D, GG>(q, k_pool, v_pool, num_blocks, num_kv_heads, bt, maxblk, \
+                                   ctx, nseq, scale, plan, out, ws, stream);
+  switch (group) {
+    PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
+    PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef PKV_CASE
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t num_q_heads,
+                       int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens) {
+  DecodePlan plan{};
+  const int32_t max_blocks = (max_context_len + 15) / 16;
+  int32_t pb;
+  if (kv_partition_tokens > 0) {
+    pb = kv_partition_tokens / 16;
+  } else {
+    const int32_t units = num_decode_seqs * num_kv_heads > 0 ? num_decode_seqs * num_kv_heads : 1;
+    const int32_t splits = (kTargetGroups + units - 1) / units;
+    pb = (max_blocks + splits - 1) / splits;
+    if (pb < kMinPartitionBlocks) pb = kMinPartitionBlocks;
+  }
+  pb = (pb + kWaves - 1) / kWaves * kWaves;
+  if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
+  if (pb < kWaves) pb = kWaves;
+  plan.partition_blocks = pb;
+  plan.max_parts = max_blocks > 0 ? (max_blocks + pb - 1) / pb : 1;
+  plan.partial_bytes = plan.max_parts > 1 ? (size_t)num_decode_seqs * num_q_heads *
+                                                plan.max_parts * (head_dim + 2) * sizeof(float)
+                                          : 0;
+  return plan;
+}
+
+hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                               int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                               int32_t head_dim, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                               void* out, void* workspace, hipStream_t stream) {
+  if (num_decode_seqs == 0) return hipSuccess;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (head_dim == 128)
+    return launch_decode_d<128>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
+                                block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
+                                scale, plan, out, workspace, stream);
+  if (head_dim == 256)
+    return launch_decode_d<256>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
+                                block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
+                                scale, plan, out, workspace, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

@@ -1,0 +1,39 @@
+// kernels.h -- host-side launchers of the HIP kernels, called by the C ABI
+// in api.hip.  Each returns hipSuccess or the launch error.  Arguments are
+// validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t num_seqs, int32_t num_tokens, int64_t* slot_mapping,
+                               hipStream_t stream);
+
+hipError_t launch_kv_append(void* k_pool, void* v_pool, int64_t num_blocks,
+                            int32_t num_kv_heads, int32_t head_dim, const void* k_new,
+                            const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                            hipStream_t stream);
+
+// Split-KV plan of the decode part of a step, made from host hints only.
+struct DecodePlan {
+  int32_t partition_blocks;  // KV blocks per partition (multiple of the waves per group)
+  int32_t max_parts;         // partitions of the longest context
+  size_t partial_bytes;      // workspace for the partials (0 when no split)
+};
+
+DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t num_q_heads,
+                       int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens);
+
+hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
+                               int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                               int32_t head_dim, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                               void* out, void* workspace, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,71 @@
+"""Step orchestration: one continuous-batching step over all layers.
+
+The batch is re-formed before every pass (deepconcepts.dev, "Continuous
+Batching Is Not a Bigger Batch", section "What the scheduler does on one
+step"), so block tables, context lengths and query offsets are step-level
+metadata shared by every layer, while the pools are per layer.  Per step:
+
+    pkv_slot_mapping                      (once)
+    for every layer:
+        pkv_kv_append                     (this layer's new K/V into its pool)
+        pkv_paged_attention_step          (decode + merge [+ prefill chunks])
+
+all enqueued on one stream; append precedes attention within a layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (KVCache, attention_workspace_size, kv_append, paged_attention_step,
+               slot_mapping)
+
+
+class Step:
+    def __init__(self, block_tables, context_lens, new_tokens, num_decode_seqs: int,
+                 num_q_heads: int, num_kv_heads: int, head_dim: int, scale: float,
+                 kv_partition_tokens: int = 0, device="cuda"):
+        import torch
+
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+        new = np.ascontiguousarray(new_tokens, dtype=np.int32)
+        self.num_seqs = int(ctx.shape[0])
+        self.num_decode_seqs = int(num_decode_seqs)
+        self.num_tokens = int(new.sum())
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.scale = float(scale)
+        self.max_context_len = int(ctx.max()) if self.num_seqs else 1
+        self.max_query_len = int(new.max()) if self.num_seqs else 1
+        self.kv_partition_tokens = int(kv_partition_tokens)
+        self.block_tables = torch.from_numpy(bt).to(device)
+        self.context_lens = torch.from_numpy(ctx).to(device)
+        pure_decode = self.num_decode_seqs == self.num_seqs
+        qsl = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+        self.query_start_loc = None if pure_decode else torch.from_numpy(qsl).to(device)
+        self.slot_mapping = torch.empty(max(self.num_tokens, 1), dtype=torch.int64, device=device)
+        ws = attention_workspace_size(self.num_seqs, self.num_decode_seqs, num_q_heads,
+                                      num_kv_heads, head_dim, self.max_context_len,
+                                      self.max_query_len, self.kv_partition_tokens)
+        self.workspace_bytes = ws
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+
+    @classmethod
+    def from_workload(cls, wl, kv_partition_tokens: int = 0, device="cuda"):
+        return cls(wl.block_tables, wl.context_lens, wl.new_tokens, wl.num_decode_seqs,
+                   wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.scale,
+                   kv_partition_tokens=kv_partition_tokens, device=device)
+
+    def plan(self, stream=None):
+        """Slot of every new token (once per step, shared by all layers)."""
+        slot_mapping(self.block_tables, self.context_lens, self.query_start_loc, self.num_tokens,
+                     self.slot_mapping, stream=stream)
+
+    def layer(self, cache: KVCache, q, k_new, v_new, out, stream=None):
+        """Append this layer's new K/V, then attend."""
+        kv_append(cache, k_new, v_new, self.slot_mapping, stream=stream)
+        paged_attention_step(cache, q, out, self.block_tables, self.context_lens,
+                             self.query_start_loc, self.num_decode_seqs, self.scale,
+                             self.max_context_len, self.max_query_len,
+                             workspace=self.workspace,
+                             kv_partition_tokens=self.kv_partition_tokens, stream=stream)
+        return out

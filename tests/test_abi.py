@@ -1,0 +1,127 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, rejects bad arguments before touching the GPU, and the
+debug validator reports each contract violation.  No GPU needed."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_decode_append_amd as pkv
+import workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(pkv_\w+)\s*\(", text))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared()
+    assert declared == set(pkv.EXPORTED)
+    for name in declared:
+        assert hasattr(pkv.lib, name), name
+
+
+def test_version_and_status_strings():
+    assert pkv.version() == 1
+    for code, name in ((0, "PKV_OK"), (-1, "PKV_ERR_INVALID_ARG"), (-2, "PKV_ERR_UNSUPPORTED"),
+                       (-3, "PKV_ERR_WORKSPACE"), (-4, "PKV_ERR_HIP"), (-5, "PKV_ERR_CONTRACT")):
+        assert pkv.status_string(code) == name
+
+
+def _cache(block_size=16, head_dim=128, kv_heads=2, blocks=10, k=FAKE, v=FAKE):
+    return pkv._Cache(k.value if k else None, v.value if v else None, blocks, block_size,
+                      kv_heads, head_dim)
+
+
+def test_append_argument_errors():
+    lib = pkv.lib
+    c = _cache()
+    assert lib.pkv_kv_append(None, FAKE, FAKE, FAKE, 4, None) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.pkv_kv_append(ctypes.byref(_cache(k=None)), FAKE, FAKE, FAKE, 4, None) == -1
+    assert lib.pkv_kv_append(ctypes.byref(_cache(block_size=32)), FAKE, FAKE, FAKE, 4, None) == -2
+    assert lib.pkv_kv_append(ctypes.byref(_cache(head_dim=96)), FAKE, FAKE, FAKE, 4, None) == -2
+    assert lib.pkv_kv_append(ctypes.byref(c), None, FAKE, FAKE, 4, None) == -1
+    assert lib.pkv_kv_append(ctypes.byref(c), FAKE, FAKE, FAKE, -1, None) == -1
+    assert lib.pkv_kv_append(ctypes.byref(c), None, None, None, 0, None) == pkv.PKV_OK  # no work
+
+
+def test_slot_mapping_argument_errors():
+    lib = pkv.lib
+    assert lib.pkv_slot_mapping(FAKE, 4, FAKE, None, 3, 3, 32, FAKE, None) == -2
+    assert lib.pkv_slot_mapping(None, 4, FAKE, None, 3, 3, 16, FAKE, None) == -1
+    assert lib.pkv_slot_mapping(FAKE, 4, FAKE, None, 3, 5, 16, FAKE, None) == -1   # T != B
+    assert lib.pkv_slot_mapping(FAKE, 0, FAKE, None, 3, 3, 16, FAKE, None) == -1
+    assert lib.pkv_slot_mapping(None, 4, None, None, 0, 0, 16, None, None) == 0
+
+
+def _step(cache, q=FAKE, out=FAKE, bt=FAKE, maxblk=64, ctx=FAKE, qsl=None, nseq=4, ndec=4, hq=12,
+          scale=0.1, mcl=1024, mql=1, part=0, ws=None, wsb=0):
+    return pkv.lib.pkv_paged_attention_step(ctypes.byref(cache), q, out, bt, maxblk, ctx, qsl, nseq,
+                                            ndec, hq, scale, mcl, mql, part, ws, wsb, None)
+
+
+def test_attention_step_argument_errors():
+    c = _cache()
+    assert _step(c, q=None) == -1
+    assert _step(c, hq=13) == -1                         # not a multiple of Hkv
+    assert _step(c, hq=18) == -2                         # group of 9 > 8
+    assert _step(_cache(head_dim=64)) == -2
+    assert _step(c, ndec=5) == -1                        # more decode seqs than seqs
+    assert _step(c, mcl=64 * 16 + 1) == -1               # longer than the table row
+    assert _step(c, part=100) == -1                      # partition not a multiple of 64
+    assert _step(c, scale=float("nan")) == -1
+    # 4 x 4096-token contexts split into partitions: workspace required
+    need = pkv.attention_workspace_size(4, 4, 12, 2, 128, 4096, 1)
+    assert need > 0
+    assert _step(c, mcl=4096, maxblk=256) == pkv.PKV_ERR_WORKSPACE
+    assert _step(c, mcl=4096, maxblk=256, ws=FAKE, wsb=need - 1) == pkv.PKV_ERR_WORKSPACE
+    assert _step(c, nseq=0, ndec=0) == pkv.PKV_OK         # empty step: nothing to do
+
+
+def test_workspace_size_is_host_only_and_monotone():
+    small = pkv.attention_workspace_size(4, 4, 12, 2, 128, 1024, 1)
+    big = pkv.attention_workspace_size(4, 4, 12, 2, 128, 65536, 1)
+    assert big >= small
+    # forcing one partition per sequence needs no workspace
+    assert pkv.attention_workspace_size(4, 4, 12, 2, 128, 1024, 1, kv_partition_tokens=1024) == 0
+    # forcing 256-token partitions of 1024 tokens: 4 partials of (d + 2) floats per row
+    assert pkv.attention_workspace_size(4, 4, 12, 2, 128, 1024, 1, kv_partition_tokens=256) == \
+        4 * 12 * 4 * (128 + 2) * 4
+    with pytest.raises(pkv.PkvError):
+        pkv.attention_workspace_size(4, 4, 12, 5, 128, 1024, 1)
+
+
+def test_validator_accepts_generated_workloads():
+    for make in (workloads.small_b4, workloads.qwen_uniform, workloads.qwen_ragged):
+        wl = make()
+        assert pkv.validate_step(wl.block_tables, wl.context_lens, wl.query_start_loc,
+                                 wl.num_decode_seqs, wl.num_blocks) == (0, -1)
+
+
+def test_validator_reports_each_violation():
+    wl = workloads.small_b4()
+    bt, ctx, qsl = wl.block_tables.copy(), wl.context_lens.copy(), wl.query_start_loc
+    v = lambda **kw: pkv.validate_step(kw.get("bt", bt), kw.get("ctx", ctx), kw.get("qsl", qsl),
+                                       kw.get("ndec", 4), kw.get("nb", wl.num_blocks),
+                                       kw.get("slots"), kw.get("mcl"), kw.get("mql"))
+    c0 = ctx.copy(); c0[1] = 0
+    assert v(ctx=c0) == (1, 1)
+    c2 = ctx.copy(); c2[0] = bt.shape[1] * 16 + 1
+    assert v(ctx=c2) == (2, 0)
+    q3 = np.array([0, 1, 3, 2, 4], np.int32)             # decreasing offsets
+    assert v(qsl=q3, ndec=1) == (3, 2)
+    b4 = bt.copy(); b4[2, 3] = wl.num_blocks
+    assert v(bt=b4) == (4, 2)
+    q5 = np.array([0, 1, 2, 3, 5], np.int32)
+    c5 = ctx.copy()
+    assert v(qsl=q5, ctx=c5) == (5, 3)
+    assert v(slots=np.array([0, 5, wl.num_blocks * 16, 7], np.int64)) == (6, 2)
+    assert v(slots=np.array([0, 5, -1, 5], np.int64)) == (7, 3)
+    assert v(mcl=100) == (8, 2)                          # ctx 256 > 100

@@ -150,9 +150,9 @@ def _build(name, layers, hq, hkv, d, ctx, new, n_dec, pool_factor, seed, pool_bl
                     block_tables=tables, seed=seed, free_blocks=free)
 
 
-def small_b4(seed: int = 0) -> Workload:
+def small_b4(seed: int = 0, layers: int = 1) -> Workload:
     ctx = [16, 64, 256, 1024]
-    return _build("small_b4", 1, 12, 2, 128, ctx, [1] * 4, 4, None, seed, pool_blocks=128)
+    return _build("small_b4", layers, 12, 2, 128, ctx, [1] * 4, 4, None, seed, pool_blocks=128)
 
 
 def qwen_uniform(seed: int = 0, batch: int = 256, ctx_len: int = 512, layers: int = 28) -> Workload:
