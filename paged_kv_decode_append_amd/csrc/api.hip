@@ -42,7 +42,7 @@ int check_step_shape(int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_he
   if (num_seqs > 0 && (max_context_len < 1 || max_query_len < 1)) return PKV_ERR_INVALID_ARG;
   if (kv_partition_tokens < 0 || kv_partition_tokens % 64 != 0 || kv_partition_tokens > 4096)
     return PKV_ERR_INVALID_ARG;
-  if (num_seqs > num_decode_seqs) return PKV_ERR_UNSUPPORTED;  // prefill chunks: not built yet
+  if (max_query_len > (1 << 30) / 64) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
 
@@ -139,16 +139,25 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
     return PKV_ERR_INVALID_ARG;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
     return PKV_ERR_INVALID_ARG;
-  (void)query_start_loc;
+  const int32_t num_prefill = num_seqs - num_decode_seqs;
+  if (num_prefill > 0 && !query_start_loc) return PKV_ERR_INVALID_ARG;
+  if (num_prefill > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, cache->num_kv_heads, num_q_heads,
                                           cache->head_dim, max_context_len, kv_partition_tokens);
   if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   if (plan.partial_bytes > 0 && (!workspace || workspace_bytes < plan.partial_bytes))
     return PKV_ERR_WORKSPACE;
-  return from_hip(pkv::launch_paged_decode(
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = from_hip(pkv::launch_paged_decode(
       q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
       cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
-      plan, out, workspace, static_cast<hipStream_t>(stream)));
+      plan, out, workspace, s));
+  if (rc != PKV_OK) return rc;
+  return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, cache->num_blocks,
+                                      cache->num_kv_heads, num_q_heads, cache->head_dim,
+                                      block_tables, max_blocks_per_seq, context_lens,
+                                      query_start_loc, num_decode_seqs, num_prefill,
+                                      max_query_len, scale, out, s));
 }
 
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,

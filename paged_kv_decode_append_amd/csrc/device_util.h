@@ -25,6 +25,11 @@ __device__ __forceinline__ uint32_t pack_h2_rtz(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 
+// Two fp32 values packed into one fp16 pair (lo = a, hi = b), round to nearest even.
+__device__ __forceinline__ uint32_t pack_h2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(f16)a, (f16)b});
+}
+
 // 2^x with the hardware v_exp_f32 (exp2(-inf) = 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

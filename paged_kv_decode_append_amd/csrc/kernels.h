@@ -36,4 +36,14 @@ hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_
                                int32_t num_decode_seqs, float scale, const DecodePlan& plan,
                                void* out, void* workspace, hipStream_t stream);
 
+// Causal attention of the prefill chunks (sequences first_seq ..
+// first_seq + num_prefill_seqs - 1) on the matrix cores.
+hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
+                          int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                          int32_t head_dim, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t first_seq,
+                          int32_t num_prefill_seqs, int32_t max_query_len, float scale,
+                          void* out, hipStream_t stream);
+
 }  // namespace pkv

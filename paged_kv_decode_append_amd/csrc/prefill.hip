@@ -1,0 +1,260 @@
+// prefill.hip -- causal attention of prefill chunks over the paged cache,
+// on the matrix cores (v_mfma_f32_16x16x32_f16).
+//
+// A prefilling sequence asks, in a pass, for the rest of its prompt capped
+// by the per-pass token budget, and shares the pass with the decoding
+// sequences (deepconcepts.dev, "Continuous Batching Is Not a Bigger Batch",
+// section "What the scheduler does on one step": chunked prefill, no
+// separate prefill phase).  Its n new tokens were just appended behind the
+// ctx - n cached ones; query row k sits at position ctx - n + k and attends
+// positions 0 .. ctx - n + k.  Unlike decode, this is a dense contraction
+// (n query rows against every key), so it runs on MFMA.
+//
+// Work-group = 4 waves = 64 query rows of one query head; wave w owns rows
+// 16w .. 16w+15.  Per tile of KV_TILE context tokens (gathered from the
+// paged pools through the block table into LDS by the whole work-group):
+//   S^T = K Q^T     A = K tile rows (LDS), B = the wave's Q rows (registers),
+//                   so each lane ends with scores of ONE query row (lane%16)
+//                   for 4 tokens per 16-token sub-tile;
+//   online softmax  per query row, base 2, row max over the 4 lanes sharing
+//                   the row; the O rescale needs no cross-lane traffic since
+//                   every lane's O values belong to its own query row;
+//   O^T += V^T P^T  B = P straight from the S^T registers (token order chosen
+//                   to match), A = V^T read from an LDS copy of the V tile
+//                   stored transposed ([d][token]), written with in-register
+//                   4x8 transposes while staging.
+// Tokens past the tile's last row position are zero-filled in LDS, so stale
+// or NaN slots never reach the MFMA accumulators; per-row causal masking is
+// a select to -inf on the scores.
+#include <algorithm>
+#include <climits>
+
+#include "device_util.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = 64;    // query rows per work-group (16 per wave)
+constexpr int kLdsPad = 8;   // fp16 padding per LDS row (bank spread)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+struct PrefillShape {
+  static constexpr int KT = D == 128 ? 64 : 32;  // context tokens per tile
+  static constexpr int NT = KT / 16;             // 16-token sub-tiles
+  static constexpr int KC = D / 32;              // 32-wide d chunks (S^T reduction)
+  static constexpr int DT = D / 16;              // 16-row d tiles of O^T
+  static constexpr int KSTRIDE = D + kLdsPad;    // K tile row stride (fp16)
+  static constexpr int VSTRIDE = KT + kLdsPad;   // V^T row stride (fp16)
+  static constexpr int LDS_BYTES = (KT * KSTRIDE + D * VSTRIDE) * 2;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_chunk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
+    const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
+    int32_t num_q_heads, const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
+    int32_t first_seq, int32_t ctx_clamp, float scale_log2, uint16_t* __restrict__ out) {
+  using S = PrefillShape<D>;
+  constexpr int KT = S::KT, NT = S::NT, KC = S::KC, DT = S::DT;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_BYTES / 2];
+  uint16_t* k_lds = lds;                         // [KT][KSTRIDE]
+  uint16_t* vt_lds = lds + KT * S::KSTRIDE;      // [D][VSTRIDE]
+
+  const int i = first_seq + blockIdx.z;
+  const int h = blockIdx.y;
+  const int g = h / (num_q_heads / num_kv_heads);
+  const int row_base = query_start_loc[i];
+  const int n = query_start_loc[i + 1] - row_base;
+  const int ctx = min(context_lens[i], ctx_clamp);
+  const int tile_row0 = blockIdx.x * kRows;
+  if (n <= 0 || tile_row0 >= n || ctx < n) return;  // uniform over the work-group
+  const int p0 = ctx - n;                            // position of the chunk's first row
+  const int pos_hi = p0 + min(tile_row0 + kRows, n) - 1;  // last position this tile needs
+  const int num_kv_tiles = pos_hi / KT + 1;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lrow = lane & 15, lgrp = lane >> 4;
+  // This lane's query row (rows past the chunk end reuse the last row; not written).
+  const int my_row_raw = tile_row0 + 16 * wave + lrow;
+  const bool row_valid = my_row_raw < n;
+  const int my_row = row_valid ? my_row_raw : n - 1;
+  const int my_pos = p0 + my_row;
+
+  // Q^T fragments: B operand, lane = query row lrow, 8 d values per 32-wide chunk.
+  f16x8 qb[KC];
+  const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + h) * D;
+#pragma unroll
+  for (int c = 0; c < KC; ++c)
+    qb[c] = *reinterpret_cast<const f16x8*>(qrow + 32 * c + 8 * lgrp);
+
+  f32x4 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_row = -__builtin_huge_valf();
+  float l_row = 0.f;
+
+  const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
+  const int64_t tile_elems = (int64_t)16 * D;
+  const int64_t head_off = (int64_t)g * tile_elems;
+  const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
+  auto token_src = [&](const uint16_t* pool, int tok) -> const uint16_t* {
+    const uint32_t b = (uint32_t)bt_row[tok >> 4];
+    const int64_t bid = b < (uint64_t)num_blocks ? b : num_blocks - 1;
+    return pool + bid * block_stride + head_off + (int64_t)(tok & 15) * D;
+  };
+
+  for (int kt = 0; kt < num_kv_tiles; ++kt) {
+    const int tok0 = kt * KT;
+    __syncthreads();  // the previous tile's LDS reads are done
+    // K tile: row-major copy, 16-byte chunks; tokens past pos_hi are zeros.
+    for (int idx = tid; idx < KT * (D / 8); idx += 256) {
+      const int tok = idx / (D / 8), ch = idx % (D / 8);
+      uint4 val = {0u, 0u, 0u, 0u};
+      if (tok0 + tok <= pos_hi)
+        val = *reinterpret_cast<const uint4*>(token_src(k_pool, tok0 + tok) + 8 * ch);
+      *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 8 * ch) = val;
+    }
+    // V tile, transposed to [d][token]: each thread moves 4 tokens x 8 d.
+    for (int grp = tid; grp < (KT / 4) * (D / 8); grp += 256) {
+      const int tq = grp % (KT / 4), dg = grp / (KT / 4);
+      uint4 v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tok = tok0 + 4 * tq + t;
+        v[t] = uint4{0u, 0u, 0u, 0u};
+        if (tok <= pos_hi) v[t] = *reinterpret_cast<const uint4*>(token_src(v_pool, tok) + 8 * dg);
+      }
+      const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+      const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+      const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+      const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        uint2 col;
+        if (j & 1) {
+          col.x = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
+          col.y = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
+        } else {
+          col.x = (w0[w] & 0xffffu) | (w1[w] << 16);
+          col.y = (w2[w] & 0xffffu) | (w3[w] << 16);
+        }
+        *reinterpret_cast<uint2*>(vt_lds + (8 * dg + j) * S::VSTRIDE + 4 * tq) = col;
+      }
+    }
+    __syncthreads();
+
+    // S^T = K Q^T: s[t][e] = score of query row lrow with token tok0 + 16t + 4*lgrp + e.
+    f32x4 s[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(k_lds + (16 * t + lrow) * S::KSTRIDE +
+                                                         32 * c + 8 * lgrp);
+        s[t] = mfma16(a, qb[c], s[t]);
+      }
+    }
+    float tile_max = -__builtin_huge_valf();
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tok0 + 16 * t + 4 * lgrp + e;
+        const float x = tok <= my_pos ? s[t][e] * scale_log2 : -__builtin_huge_valf();
+        s[t][e] = x;
+        tile_max = fmaxf(tile_max, x);
+      }
+    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 16));
+    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+    const float m_new = fmaxf(m_row, tile_max);  // finite: token 0 is visible to every row
+    const float alpha = fast_exp2(m_row - m_new);
+    m_row = m_new;
+    l_row *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[t] *= alpha;
+
+    // P^T as B operands: chunk c2 covers sub-tiles 2*c2 (elements 0..3) and 2*c2+1 (4..7).
+    f16x8 pb[NT / 2];
+#pragma unroll
+    for (int c2 = 0; c2 < NT / 2; ++c2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(s[2 * c2 + e / 4][e % 4] - m_new);
+        pb[c2][e] = (f16)p;
+        l_row += (float)pb[c2][e];
+      }
+
+    // O^T += V^T P^T; A lane = d row 16*dt + lrow, tokens matching pb's order.
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int c2 = 0; c2 < NT / 2; ++c2) {
+        const uint16_t* vrow = vt_lds + (16 * dt + lrow) * S::VSTRIDE + 32 * c2 + 4 * lgrp;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
+        o[dt] = mfma16(__builtin_bit_cast(f16x8, packed), pb[c2], o[dt]);
+      }
+  }
+
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  if (!row_valid) return;
+  const float inv = 1.f / l_row;
+  uint16_t* dst = out + ((int64_t)(row_base + my_row) * num_q_heads + h) * D + 4 * lgrp;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    uint2 w;
+    w.x = pack_h2_rne(o[dt][0] * inv, o[dt][1] * inv);
+    w.y = pack_h2_rne(o[dt][2] * inv, o[dt][3] * inv);
+    *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
+                          int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                          int32_t head_dim, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start_loc, int32_t first_seq,
+                          int32_t num_prefill_seqs, int32_t max_query_len, float scale,
+                          void* out, hipStream_t stream) {
+  if (num_prefill_seqs <= 0) return hipSuccess;
+  const int32_t ctx_clamp =
+      (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
+  const dim3 grid((max_query_len + kRows - 1) / kRows, num_q_heads, num_prefill_seqs);
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  if (head_dim == 128)
+    hipLaunchKernelGGL(prefill_chunk_kernel<128>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                       query_start_loc, first_seq, ctx_clamp, scale * kLog2e,
+                       static_cast<uint16_t*>(out));
+  else if (head_dim == 256)
+    hipLaunchKernelGGL(prefill_chunk_kernel<256>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                       query_start_loc, first_seq, ctx_clamp, scale * kLog2e,
+                       static_cast<uint16_t*>(out));
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -65,12 +65,15 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison: bool = True,
-                        seq_subset=None, tensors=None):
+                        seq_subset=None, tensors=None, row_samples=None):
     """One layer of one step on the GPU, checked against the oracle.
 
     Checks: slot mapping bit-exact; whole pools after the append bit-exact
     (canaries and NaN poison included); attention within tolerance for the
-    sequences in seq_subset (all when None).  Returns (out_fp16, ref, errors).
+    sequences in seq_subset (all when None), and for row_samples
+    {sequence: [chunk rows]} of long prefill chunks, each sampled row checked
+    as the query that attends positions [0, its position] through the same
+    block table.  Returns (out_fp16, ref, errors).
     """
     t = workloads_tensors(wl, layer) if tensors is None else tensors
     if poison:
@@ -93,11 +96,23 @@ def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison
     assert np.array_equal(host_bits(t["k_pool"]), kp_ref), "K pool after append"
     assert np.array_equal(host_bits(t["v_pool"]), vp_ref), "V pool after append"
 
-    ref = oracle.paged_attention(q, kp_ref, vp_ref, wl.block_tables, wl.context_lens, qsl,
-                                 wl.scale, seq_subset=seq_subset)
     got = out.cpu().numpy()
-    rows = rows_of(wl, seq_subset)
-    errs = assert_close(got[rows], ref[rows], wl.name)
+    ref = None
+    errs = (0.0, 0.0)
+    if seq_subset is None or len(seq_subset):
+        ref = oracle.paged_attention(q, kp_ref, vp_ref, wl.block_tables, wl.context_lens, qsl,
+                                     wl.scale, seq_subset=seq_subset)
+        rows = rows_of(wl, seq_subset)
+        errs = assert_close(got[rows], ref[rows], wl.name)
+    for seq, sample in (row_samples or {}).items():
+        sample = np.asarray(sample)
+        n, ctx, r0 = wl.new_tokens[seq], wl.context_lens[seq], wl.query_start_loc[seq]
+        sub_ctx = (ctx - n + sample + 1).astype(np.int32)
+        sub_bt = np.repeat(wl.block_tables[seq:seq + 1], len(sample), axis=0)
+        sub_ref = oracle.paged_attention(q[r0 + sample], kp_ref, vp_ref, sub_bt, sub_ctx, None,
+                                         wl.scale)
+        e2 = assert_close(got[r0 + sample], sub_ref, f"{wl.name} rows of sequence {seq}")
+        errs = (max(errs[0], e2[0]), max(errs[1], e2[1]))
     return got, ref, errs
 
 
