@@ -46,6 +46,13 @@ int check_step_shape(int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_he
   return PKV_OK;
 }
 
+// Workspace: decode partials first, then prefill partials (256-byte aligned).
+size_t prefill_offset(const pkv::DecodePlan& d) { return (d.partial_bytes + 255) / 256 * 256; }
+
+size_t workspace_layout(const pkv::DecodePlan& d, const pkv::PrefillPlan& p) {
+  return p.partial_bytes > 0 ? prefill_offset(d) + p.partial_bytes : d.partial_bytes;
+}
+
 thread_local hipError_t t_last_hip_error = hipSuccess;
 
 int from_hip(hipError_t e) {
@@ -116,7 +123,9 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, num_kv_heads, num_q_heads, head_dim,
                                           max_context_len, kv_partition_tokens);
   if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
-  *bytes = plan.partial_bytes;
+  const pkv::PrefillPlan pplan = pkv::plan_prefill(num_seqs - num_decode_seqs, num_q_heads,
+                                                   head_dim, max_context_len, max_query_len);
+  *bytes = workspace_layout(plan, pplan);
   return PKV_OK;
 }
 
@@ -145,8 +154,11 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, cache->num_kv_heads, num_q_heads,
                                           cache->head_dim, max_context_len, kv_partition_tokens);
   if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
-  if (plan.partial_bytes > 0 && (!workspace || workspace_bytes < plan.partial_bytes))
-    return PKV_ERR_WORKSPACE;
+  const pkv::PrefillPlan pplan = pkv::plan_prefill(num_prefill, num_q_heads, cache->head_dim,
+                                                   max_context_len, max_query_len);
+  const size_t need = workspace_layout(plan, pplan);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   rc = from_hip(pkv::launch_paged_decode(
       q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
@@ -157,7 +169,7 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
                                       cache->num_kv_heads, num_q_heads, cache->head_dim,
                                       block_tables, max_blocks_per_seq, context_lens,
                                       query_start_loc, num_decode_seqs, num_prefill,
-                                      max_query_len, scale, out, s));
+                                      max_query_len, scale, pplan, out, prefill_ws, s));
 }
 
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -354,40 +354,53 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   }
 }
 
-// One wave per (sequence, query head) with more than one partition.
+// One work-group per (sequence, query head) with more than one partition:
+// the 4 waves take every 4th partition, then combine through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
-    int32_t max_parts, int32_t num_q_heads, int32_t num_rows, uint16_t* __restrict__ out) {
+    int32_t max_parts, int32_t num_q_heads, uint16_t* __restrict__ out) {
   constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row_head = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row_head >= num_rows) return;
+  __shared__ float s_max[4];
+  __shared__ float s_w[4];
+  __shared__ float s_acc[4][D];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row_head = blockIdx.x;
   const int i = row_head / num_q_heads;
   const int nblk = (min(context_lens[i], ctx_clamp) + 15) >> 4;
   const int np = (nblk + partition_blocks - 1) / partition_blocks;
-  if (np <= 1) return;
+  if (np <= 1) return;  // written directly by the decode kernel
   const float* ml = part_ml + (int64_t)row_head * max_parts * 2;
   const float* po = part_o + (int64_t)row_head * max_parts * D + EPL * lane;
 
   float M = -__builtin_huge_valf();
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[2 * p]);
+  for (int p = tid; p < np; p += 256) M = fmaxf(M, ml[2 * p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) s_max[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 
-  float W = 0.f, o[EPL];
+  float W = 0.f, acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int p = 0; p < np; ++p) {
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int p = wave; p < np; p += 4) {
     const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
     W += w;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += w * po[(int64_t)p * D + e];
+    for (int e = 0; e < EPL; ++e) acc[e] += w * po[(int64_t)p * D + e];
   }
-  uint16_t* dst = out + (int64_t)row_head * D + EPL * lane;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = __builtin_bit_cast(uint16_t, (f16)(o[e] / W));
+  for (int e = 0; e < EPL; ++e) s_acc[wave][EPL * lane + e] = acc[e];
+  if (lane == 0) s_w[wave] = W;
+  __syncthreads();
+  if (tid < D) {
+    const float total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    const float o = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
+    out[(int64_t)row_head * D + tid] = __builtin_bit_cast(uint16_t, (f16)(o / total));
+  }
 }
 
 template <int D, int G>
@@ -415,10 +428,9 @@ hipError_t launch_decode_dg(const void* q, const void* k_pool, const void* v_poo
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
   const int32_t rows = num_decode_seqs * num_q_heads;
-  (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((lse_merge_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream, part_o,
-                     part_ml, context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts,
-                     num_q_heads, rows, static_cast<uint16_t*>(out));
+  hipLaunchKernelGGL((lse_merge_kernel<D>), dim3(rows), dim3(256), 0, stream, part_o, part_ml,
+                     context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts, num_q_heads,
+                     static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -36,6 +36,17 @@ hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_
                                int32_t num_decode_seqs, float scale, const DecodePlan& plan,
                                void* out, void* workspace, hipStream_t stream);
 
+// Split-KV plan of the prefill chunks: each 64-row query tile is cut into
+// `splits` ranges of context tiles, merged by log-sum-exp when splits > 1.
+struct PrefillPlan {
+  int32_t splits;
+  int64_t max_row_heads;   // bound on (prefill rows x query heads)
+  size_t partial_bytes;
+};
+
+PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t max_query_len);
+
 // Causal attention of the prefill chunks (sequences first_seq ..
 // first_seq + num_prefill_seqs - 1) on the matrix cores.
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
@@ -44,6 +55,7 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t first_seq,
                           int32_t num_prefill_seqs, int32_t max_query_len, float scale,
-                          void* out, hipStream_t stream);
+                          const PrefillPlan& plan, void* out, void* workspace,
+                          hipStream_t stream);
 
 }  // namespace pkv

@@ -40,6 +40,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 64;    // query rows per work-group (16 per wave)
+constexpr int64_t kResidentGroups = 512;  // 256 CUs x 2 work-groups resident per CU
+constexpr uint32_t kXcds = 8;
+constexpr int64_t kMaxPrefillSplits = 16;
 constexpr int kLdsPad = 8;   // fp16 padding per LDS row (bank spread)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -58,15 +61,24 @@ struct PrefillShape {
   static constexpr int LDS_BYTES = (KT * KSTRIDE + D * VSTRIDE) * 2;
 };
 
+// One thread's share of a K/V tile in flight: 4 K chunks of 16 bytes, and
+// 4 tokens x 8 d values of V (one 4x8 group per thread).
+struct TileRegs {
+  uint4 k[4];
+  uint4 v[4];
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
     int32_t num_q_heads, const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
-    int32_t first_seq, int32_t ctx_clamp, float scale_log2, uint16_t* __restrict__ out) {
+    int32_t first_seq, int32_t ctx_clamp, int32_t num_splits, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = PrefillShape<D>;
   constexpr int KT = S::KT, NT = S::NT, KC = S::KC, DT = S::DT;
+  static_assert(KT * (D / 8) == 4 * 256 && (KT / 4) * (D / 8) == 256, "tile split over 256 threads");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_BYTES / 2];
   uint16_t* k_lds = lds;                         // [KT][KSTRIDE]
   uint16_t* vt_lds = lds + KT * S::KSTRIDE;      // [D][VSTRIDE]
@@ -74,14 +86,18 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   const int i = first_seq + blockIdx.z;
   const int h = blockIdx.y;
   const int g = h / (num_q_heads / num_kv_heads);
+  const int split = blockIdx.x % num_splits;
+  const int tile_row0 = (blockIdx.x / num_splits) * kRows;  // x past the last tile: exits below
   const int row_base = query_start_loc[i];
   const int n = query_start_loc[i + 1] - row_base;
   const int ctx = min(context_lens[i], ctx_clamp);
-  const int tile_row0 = blockIdx.x * kRows;
   if (n <= 0 || tile_row0 >= n || ctx < n) return;  // uniform over the work-group
   const int p0 = ctx - n;                            // position of the chunk's first row
   const int pos_hi = p0 + min(tile_row0 + kRows, n) - 1;  // last position this tile needs
   const int num_kv_tiles = pos_hi / KT + 1;
+  const int per_split = (num_kv_tiles + num_splits - 1) / num_splits;
+  const int kt_begin = split * per_split;
+  const int kt_end = min(kt_begin + per_split, num_kv_tiles);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
@@ -108,51 +124,73 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   const int64_t tile_elems = (int64_t)16 * D;
   const int64_t head_off = (int64_t)g * tile_elems;
   const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
-  auto token_src = [&](const uint16_t* pool, int tok) -> const uint16_t* {
-    const uint32_t b = (uint32_t)bt_row[tok >> 4];
-    const int64_t bid = b < (uint64_t)num_blocks ? b : num_blocks - 1;
-    return pool + bid * block_stride + head_off + (int64_t)(tok & 15) * D;
+  const int used_blocks = (pos_hi >> 4) + 1;  // table entries this tile range may read
+  // Global -> registers for tile kt; tokens past pos_hi are zeros.  The tile's
+  // KT/16 block ids are work-group uniform (scalar loads), clamped into the pool.
+  auto load_tile = [&](TileRegs& r, int kt) {
+    const int tok0 = kt * KT;
+    int64_t tile_base[KT / 16];
+#pragma unroll
+    for (int b = 0; b < KT / 16; ++b) {
+      const int j = kt * (KT / 16) + b;
+      const uint32_t id = j < used_blocks ? (uint32_t)bt_row[j] : 0u;
+      tile_base[b] = (int64_t)(id < (uint64_t)num_blocks ? id : num_blocks - 1) * block_stride +
+                     head_off;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      const int tok = idx / (D / 8), ch = idx % (D / 8);
+      r.k[j] = uint4{0u, 0u, 0u, 0u};
+      if (tok0 + tok <= pos_hi)
+        r.k[j] = *reinterpret_cast<const uint4*>(k_pool + tile_base[tok >> 4] +
+                                                 (tok & 15) * D + 8 * ch);
+    }
+    const int tq = tid % (KT / 4), dg = tid / (KT / 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = 4 * tq + t;
+      r.v[t] = uint4{0u, 0u, 0u, 0u};
+      if (tok0 + tok <= pos_hi)
+        r.v[t] = *reinterpret_cast<const uint4*>(v_pool + tile_base[tok >> 4] + (tok & 15) * D +
+                                                 8 * dg);
+    }
+  };
+  // Registers -> LDS: K row-major, V transposed to [d][token] (4x8 transpose).
+  auto store_tile = [&](const TileRegs& r) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = tid + 256 * j;
+      const int tok = idx / (D / 8), ch = idx % (D / 8);
+      *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 8 * ch) = r.k[j];
+    }
+    const int tq = tid % (KT / 4), dg = tid / (KT / 4);
+    const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+    const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+    const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
+    const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = j >> 1;
+      uint2 col;
+      if (j & 1) {
+        col.x = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
+        col.y = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
+      } else {
+        col.x = (w0[w] & 0xffffu) | (w1[w] << 16);
+        col.y = (w2[w] & 0xffffu) | (w3[w] << 16);
+      }
+      *reinterpret_cast<uint2*>(vt_lds + (8 * dg + j) * S::VSTRIDE + 4 * tq) = col;
+    }
   };
 
-  for (int kt = 0; kt < num_kv_tiles; ++kt) {
+  TileRegs next;
+  if (kt_begin < kt_end) load_tile(next, kt_begin);
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int tok0 = kt * KT;
     __syncthreads();  // the previous tile's LDS reads are done
-    // K tile: row-major copy, 16-byte chunks; tokens past pos_hi are zeros.
-    for (int idx = tid; idx < KT * (D / 8); idx += 256) {
-      const int tok = idx / (D / 8), ch = idx % (D / 8);
-      uint4 val = {0u, 0u, 0u, 0u};
-      if (tok0 + tok <= pos_hi)
-        val = *reinterpret_cast<const uint4*>(token_src(k_pool, tok0 + tok) + 8 * ch);
-      *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 8 * ch) = val;
-    }
-    // V tile, transposed to [d][token]: each thread moves 4 tokens x 8 d.
-    for (int grp = tid; grp < (KT / 4) * (D / 8); grp += 256) {
-      const int tq = grp % (KT / 4), dg = grp / (KT / 4);
-      uint4 v[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int tok = tok0 + 4 * tq + t;
-        v[t] = uint4{0u, 0u, 0u, 0u};
-        if (tok <= pos_hi) v[t] = *reinterpret_cast<const uint4*>(token_src(v_pool, tok) + 8 * dg);
-      }
-      const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-      const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-      const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-      const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        uint2 col;
-        if (j & 1) {
-          col.x = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
-          col.y = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
-        } else {
-          col.x = (w0[w] & 0xffffu) | (w1[w] << 16);
-          col.y = (w2[w] & 0xffffu) | (w3[w] << 16);
-        }
-        *reinterpret_cast<uint2*>(vt_lds + (8 * dg + j) * S::VSTRIDE + 4 * tq) = col;
-      }
-    }
+    store_tile(next);
+    if (kt + 1 < kt_end) load_tile(next, kt + 1);  // in flight during this tile's math
     __syncthreads();
 
     // S^T = K Q^T: s[t][e] = score of query row lrow with token tok0 + 16t + 4*lgrp + e.
@@ -179,8 +217,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
       }
     tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 16));
     tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
-    const float m_new = fmaxf(m_row, tile_max);  // finite: token 0 is visible to every row
-    const float alpha = fast_exp2(m_row - m_new);
+    const float m_new = fmaxf(m_row, tile_max);
+    // A row that has seen no visible token yet keeps weight 0 (no -inf - -inf).
+    const float m_ref = m_new == -__builtin_huge_valf() ? 0.f : m_new;
+    const float alpha = fast_exp2(m_row - m_ref);
     m_row = m_new;
     l_row *= alpha;
 #pragma unroll
@@ -192,7 +232,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     for (int c2 = 0; c2 < NT / 2; ++c2)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(s[2 * c2 + e / 4][e % 4] - m_new);
+        const float p = fast_exp2(s[2 * c2 + e / 4][e % 4] - m_ref);
         pb[c2][e] = (f16)p;
         l_row += (float)pb[c2][e];
       }
@@ -213,18 +253,124 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   l_row += __shfl_xor(l_row, 16);
   l_row += __shfl_xor(l_row, 32);
   if (!row_valid) return;
-  const float inv = 1.f / l_row;
-  uint16_t* dst = out + ((int64_t)(row_base + my_row) * num_q_heads + h) * D + 4 * lgrp;
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + h;
+  if (num_splits == 1) {
+    uint16_t* dst = out + row_head * D + 4 * lgrp;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    uint2 w;
-    w.x = pack_h2_rne(o[dt][0] * inv, o[dt][1] * inv);
-    w.y = pack_h2_rne(o[dt][2] * inv, o[dt][3] * inv);
-    *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+    for (int dt = 0; dt < DT; ++dt) {
+      uint2 w;
+      w.x = pack_h2_rne(o[dt][0] * inv, o[dt][1] * inv);
+      w.y = pack_h2_rne(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+    }
+    return;
+  }
+  // Partial of this split: (o / l, m, l); l = 0 when no position was visible.
+  const int64_t first_row = query_start_loc[first_seq];
+  const int64_t pidx = ((row_base + my_row - first_row) * num_q_heads + h) * num_splits + split;
+  float* dst = part_o + pidx * D + 4 * lgrp;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt] * inv;
+  if (lane < 16) {
+    part_ml[pidx * 2] = m_row;
+    part_ml[pidx * 2 + 1] = l_row;
   }
 }
 
+// Merge of the splits of every (prefill row, query head): one wave each.
+//   M = max m_s over splits with l_s > 0, w_s = l_s 2^(m_s - M),
+//   O = sum_s w_s o_s / sum_s w_s.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ query_start_loc, int32_t first_seq, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_splits, int64_t max_row_heads, uint16_t* __restrict__ out) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t first_row = query_start_loc[first_seq];
+  const int64_t rows = (int64_t)query_start_loc[num_seqs] - first_row;
+  if (rh >= rows * num_q_heads || rh >= max_row_heads) return;
+  const float* ml = part_ml + rh * num_splits * 2;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < num_splits; ++s)
+    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
+  float W = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int s = 0; s < num_splits; ++s) {
+    const float l = ml[2 * s + 1];
+    if (!(l > 0.f)) continue;
+    const float w = l * fast_exp2(ml[2 * s] - M);
+    W += w;
+    const float* src = part_o + (rh * num_splits + s) * D + EPL * lane;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
+  }
+  uint16_t* dst = out + (first_row * num_q_heads + rh) * D + EPL * lane;
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = __builtin_bit_cast(uint16_t, (f16)(acc[e] * inv));
+}
+
 }  // namespace
+
+PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t max_query_len) {
+  PrefillPlan plan{};
+  plan.splits = 1;
+  if (num_prefill_seqs <= 0) return plan;
+  const int32_t kt = head_dim == 128 ? PrefillShape<128>::KT : PrefillShape<256>::KT;
+  const int64_t groups =
+      (int64_t)num_prefill_seqs * ((max_query_len + kRows - 1) / kRows) * num_q_heads;
+  const int64_t kv_tiles = (max_context_len + kt - 1) / kt;
+  // as many splits as fit in one round of resident work-groups (no tail round)
+  int64_t splits = kResidentGroups / groups;
+  splits = std::min<int64_t>(std::min<int64_t>(splits, kMaxPrefillSplits), kv_tiles);
+  plan.splits = (int32_t)std::max<int64_t>(splits, 1);
+  plan.max_row_heads = (int64_t)num_prefill_seqs * max_query_len * num_q_heads;
+  plan.partial_bytes =
+      plan.splits > 1 ? (size_t)plan.max_row_heads * plan.splits * (head_dim + 2) * sizeof(float)
+                      : 0;
+  return plan;
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void* v_pool,
+                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, const int32_t* query_start_loc,
+                                   int32_t first_seq, int32_t num_prefill_seqs,
+                                   int32_t max_query_len, float scale, const PrefillPlan& plan,
+                                   void* out, void* workspace, hipStream_t stream) {
+  const int32_t ctx_clamp =
+      (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml = part_o ? part_o + (size_t)plan.max_row_heads * plan.splits * D : nullptr;
+  // x = (query tile, split), padded to a multiple of the 8 XCDs: work-groups
+  // are dealt round-robin over the XCDs, so every head of one (tile, split)
+  // -- in particular the G heads sharing one KV head -- runs on one XCD and
+  // reads the K/V tiles through the same L2.
+  const uint32_t x = ((max_query_len + kRows - 1) / kRows) * plan.splits;
+  const dim3 grid((x + kXcds - 1) / kXcds * kXcds, num_q_heads, num_prefill_seqs);
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  hipLaunchKernelGGL(prefill_chunk_kernel<D>, grid, dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                     static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads, num_q_heads,
+                     block_tables, max_blocks_per_seq, context_lens, query_start_loc, first_seq,
+                     ctx_clamp, plan.splits, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
+                     part_ml);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.splits == 1) return err;
+  const int64_t waves = plan.max_row_heads;
+  hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0,
+                     stream, part_o, part_ml, query_start_loc, first_seq,
+                     first_seq + num_prefill_seqs, num_q_heads, plan.splits, plan.max_row_heads,
+                     static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
@@ -232,29 +378,20 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start_loc, int32_t first_seq,
                           int32_t num_prefill_seqs, int32_t max_query_len, float scale,
-                          void* out, hipStream_t stream) {
+                          const PrefillPlan& plan, void* out, void* workspace,
+                          hipStream_t stream) {
   if (num_prefill_seqs <= 0) return hipSuccess;
-  const int32_t ctx_clamp =
-      (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
-  const dim3 grid((max_query_len + kRows - 1) / kRows, num_q_heads, num_prefill_seqs);
-  (void)hipGetLastError();  // drop errors left by earlier runtime calls
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_chunk_kernel<128>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
-                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
-                       query_start_loc, first_seq, ctx_clamp, scale * kLog2e,
-                       static_cast<uint16_t*>(out));
-  else if (head_dim == 256)
-    hipLaunchKernelGGL(prefill_chunk_kernel<256>, grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
-                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
-                       query_start_loc, first_seq, ctx_clamp, scale * kLog2e,
-                       static_cast<uint16_t*>(out));
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+    return launch_prefill_d<128>(q, k_pool, v_pool, num_blocks, num_kv_heads, num_q_heads,
+                                 block_tables, max_blocks_per_seq, context_lens,
+                                 query_start_loc, first_seq, num_prefill_seqs, max_query_len,
+                                 scale, plan, out, workspace, stream);
+  if (head_dim == 256)
+    return launch_prefill_d<256>(q, k_pool, v_pool, num_blocks, num_kv_heads, num_q_heads,
+                                 block_tables, max_blocks_per_seq, context_lens,
+                                 query_start_loc, first_seq, num_prefill_seqs, max_query_len,
+                                 scale, plan, out, workspace, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv
