@@ -43,7 +43,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
-    ap.add_argument("--partition", type=int, default=0, help="force split-KV partition tokens")
+    ap.add_argument("--batch", type=int, default=0, help="override the batch (uniform / long_context)")
+    ap.add_argument("--ctx", type=int, default=0, help="override the context length (uniform / long_context)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="force split-KV partition tokens (multiple of 64; 0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     return ap.parse_args()
@@ -104,7 +107,9 @@ def main():
         sys.exit(1)
 
     make = workloads.WORKLOADS[args.workload]
-    wl = make(layers=args.layers) if args.layers else make()
+    overrides = {k: v for k, v in (("layers", args.layers), ("batch", args.batch),
+                                    ("ctx_len", args.ctx)) if v}
+    wl = make(**overrides)
     layers = [workloads.layer_tensors(wl, l, device="cuda") for l in range(wl.num_layers)]
     caches = [pkv.KVCache(t["k_pool"], t["v_pool"]) for t in layers]
     outs = [torch.empty_like(t["q"]) for t in layers]

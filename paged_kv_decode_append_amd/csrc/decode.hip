@@ -9,20 +9,25 @@
 // real tokens, so a ragged mix does not pay for its widest member).
 //
 // Work decomposition (gfx950, wave64):
-//   grid = (sequence, KV head, partition); a work-group of 4 waves reads the
-//   partition's blocks of ONE KV head once and applies them to all G query
-//   heads of that group (grouped-query attention), so every K/V byte leaves
-//   HBM once per step.
-//   Blocks of the partition are dealt round-robin to the waves; each wave
-//   prefetches its next block into registers while it computes the current
-//   one, and fetches all its block ids with one vector load up front.
+//   grid = (sequence, KV head, partition of the context); a work-group of 4
+//   waves reads the partition's blocks of ONE KV head once and applies them
+//   to all G query heads of that group (grouped-query attention), so every
+//   K/V byte leaves HBM once per step.  Work-groups are dispatched highest
+//   partition first: only long contexts have high partitions, so the
+//   longest work starts first and short sequences fill the gaps behind it
+//   (longest-first list scheduling by the hardware dispatcher).
+//   Blocks of a partition are dealt round-robin to its waves; each wave
+//   fetches all its block ids with one vector load and keeps about 16 KiB of
+//   K/V in flight: at d = 128 block f+8 is loaded into block f's registers
+//   in two halves (K once f's scores are done, V after f's P.V), at d = 256
+//   one block (16 KiB) is loaded ahead into a second buffer.
 //
 // Per block (16 tokens x d) and wave:
 //   K layout: D/16 lanes share one token row, each lane holding 16 of its
 //     d values (two 16-byte chunks), so a K load instruction reads whole
 //     128-byte runs of rows.  q.k is 8 packed fp16 dot products
-//     (v_dot2_f32_f16, fp32 accumulate) per head, then a DPP butterfly
-//     inside the lane group.
+//     (v_dot2_f32_f16, fp32 accumulate) per head with the query fragments
+//     read from LDS, then a DPP butterfly inside the lane group.
 //   Online softmax, base 2: scores are scaled by scale*log2(e); the running
 //     max m is wave-uniform and only raised when a score exceeds it by more
 //     than 8 (then the accumulators are rescaled), so weights p = 2^(s-m)
@@ -51,8 +56,9 @@ namespace {
 constexpr int kWaves = 4;                 // waves per work-group
 constexpr int kMaxBlocksPerWave = 64;     // one block id per lane
 constexpr int kMaxPartitionBlocks = kWaves * kMaxBlocksPerWave;
-constexpr int kTargetGroups = 512;        // work-groups that keep 256 CUs busy
-constexpr int kMinPartitionBlocks = 16;   // 256 tokens
+constexpr int32_t kResidentGroups = 512;  // 256 CUs x 2 work-groups of 4 waves
+constexpr int32_t kTargetItems = 1024;    // work-groups to aim for when contexts must be cut
+constexpr int32_t kMinPartitionBlocks = 16;
 constexpr float kRescaleSlack = 8.f;      // lazy max: rescale only past m + 8 (base 2)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -77,8 +83,7 @@ struct WaveState {
 };
 
 template <int D>
-__device__ __forceinline__ void load_kv(KVRegs<D>& r, const uint16_t* __restrict__ ktile,
-                                        const uint16_t* __restrict__ vtile, int lane) {
+__device__ __forceinline__ void load_k(KVRegs<D>& r, const uint16_t* __restrict__ ktile, int lane) {
   constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
   const int tl = lane / LPT, c = lane % LPT;
 #pragma unroll
@@ -87,6 +92,10 @@ __device__ __forceinline__ void load_kv(KVRegs<D>& r, const uint16_t* __restrict
     for (int ch = 0; ch < 2; ++ch)
       r.k[s][ch] =
           *reinterpret_cast<const uint4*>(ktile + (tl + TPS * s) * D + 8 * (c + LPT * ch));
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(KVRegs<D>& r, const uint16_t* __restrict__ vtile, int lane) {
 #pragma unroll
   for (int t = 0; t < 16; ++t)
     r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
@@ -119,10 +128,14 @@ __device__ __forceinline__ void pv_dword(float (&acc)[G][2], const uint32_t (&pr
   }
 }
 
-// One 16-token block: scores, lazy-max online softmax, P.V.
+// One 16-token block, first half: scores from the K registers, lazy-max
+// online softmax, weights to the wave's LDS buffer.  After it returns the K
+// registers are free (the next K load may target them).
 // tok0 = logical position of the block's first token.
+// qs = the segment's G query rows in LDS ([G][D] fp16); each lane reads its
+// 16-value fragments per block instead of holding them in registers.
 template <int D, int G>
-__device__ __forceinline__ void attend_block(KVRegs<D>& r, const uint32_t (&q)[G][8],
+__device__ __forceinline__ void block_scores(const KVRegs<D>& r, const uint16_t* qs,
                                              WaveState<D, G>& st, int tok0, int ctx,
                                              float scale_log2, uint32_t* __restrict__ p_lds,
                                              int lane) {
@@ -131,14 +144,19 @@ __device__ __forceinline__ void attend_block(KVRegs<D>& r, const uint32_t (&q)[G
   const int tl = lane / LPT, c = lane % LPT;
   const bool tail = tok0 + 16 > ctx;
   const float kNegInf = -__builtin_huge_valf();
+  asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
 
   // Scores of this lane group's SPB tokens (tl + TPS*s) for every head.
   float x[SPB][G];
 #pragma unroll
-  for (int s = 0; s < SPB; ++s)
+  for (int h = 0; h < G; ++h) {
+    const uint4 qa = *reinterpret_cast<const uint4*>(qs + h * D + 8 * c);
+    const uint4 qb = *reinterpret_cast<const uint4*>(qs + h * D + 8 * (c + LPT));
+    const uint32_t qh[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-      x[s][h] = group_sum<LPT>(dot16(q[h], r.k[s][0], r.k[s][1])) * scale_log2;
+    for (int s = 0; s < SPB; ++s)
+      x[s][h] = group_sum<LPT>(dot16(qh, r.k[s][0], r.k[s][1])) * scale_log2;
+  }
   if (tail) {
 #pragma unroll
     for (int s = 0; s < SPB; ++s) {
@@ -190,8 +208,16 @@ __device__ __forceinline__ void attend_block(KVRegs<D>& r, const uint32_t (&q)[G
       for (int h = 0; h < G; ++h) p_lds[(j * TPS + tl) * GP + h] = pp[j][h];
   }
   wave_fence();
+}
 
-  if (tail) {
+// Second half: P.V from the V registers and the weights in LDS.  Rows of
+// positions >= ctx are zeroed first (select), so stale slots never leak.
+template <int D, int G>
+__device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int tok0, int ctx,
+                                         const uint32_t* __restrict__ p_lds) {
+  constexpr int TPS = KVRegs<D>::TPS;
+  constexpr int GP = (G + 3) & ~3;
+  if (tok0 + 16 > ctx) {
 #pragma unroll
     for (int t = 0; t < 16; ++t)
       if (tok0 + t >= ctx) r.v[t] = typename VFrag<D>::T{};
@@ -225,6 +251,7 @@ __device__ __forceinline__ void attend_block(KVRegs<D>& r, const uint32_t (&q)[G
   wave_fence();
 }
 
+
 template <int D, int G>
 __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
@@ -234,12 +261,18 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   constexpr int LPT = D / 16, EPL = D / 64, GP = (G + 3) & ~3;
+  // d = 128: two blocks (16 KiB) in flight per wave by refilling a buffer as
+  // soon as each half is consumed; d = 256: one block is already 16 KiB, and
+  // the plain two-buffer scheme keeps registers under 256 (2 waves per SIMD).
+  constexpr bool kEarlyRefill = D == 128;
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ uint32_t s_p[kWaves][8 * GP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
 
-  const int i = blockIdx.x, g = blockIdx.y, part = blockIdx.z;
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
   // A length beyond the table row or the planned partitions breaks the
   // caller contract; clamp so that it can only give wrong numbers.
@@ -249,8 +282,16 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   if (ctx <= 0 || b0 >= nblk) return;  // uniform over the work-group
   const int b1 = min(b0 + partition_blocks, nblk);
   const int nparts = (nblk + partition_blocks - 1) / partition_blocks;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = lane % LPT;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // Query rows of the G heads -> LDS (issued first; used after the barrier).
+  const uint4* qsrc =
+      reinterpret_cast<const uint4*>(q + ((int64_t)i * num_q_heads + (int64_t)g * G) * D);
+  constexpr int QCH = G * D / 8;
+  uint4 qstage[(QCH + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (QCH + 255) / 256; ++k)
+    if (tid + 256 * k < QCH) qstage[k] = qsrc[tid + 256 * k];
 
   // Block ids of this wave's blocks b0 + wave + kWaves*k, one per lane,
   // clamped into the pool.
@@ -261,17 +302,28 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     const uint32_t b = (uint32_t)bt_row[b0 + wave + kWaves * lane];
     my_bid = (int)(b < (uint64_t)num_blocks ? b : (uint32_t)(num_blocks - 1));
   }
+  const int64_t tile_elems = (int64_t)16 * D;
+  const int64_t head_off = (int64_t)g * tile_elems;
+  const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
+  auto tile_off = [&](int k) -> int64_t {
+    return (int64_t)__builtin_amdgcn_readlane(my_bid, k) * block_stride + head_off;
+  };
 
-  // Query fragments of the G heads in the K layout.
-  uint32_t qf[G][8];
-  const uint16_t* qrow = q + ((int64_t)i * num_q_heads + (int64_t)g * G) * D;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 a = *reinterpret_cast<const uint4*>(qrow + h * D + 8 * c);
-    const uint4 b = *reinterpret_cast<const uint4*>(qrow + h * D + 8 * (c + LPT));
-    qf[h][0] = a.x; qf[h][1] = a.y; qf[h][2] = a.z; qf[h][3] = a.w;
-    qf[h][4] = b.x; qf[h][5] = b.y; qf[h][6] = b.z; qf[h][7] = b.w;
+  KVRegs<D> A, B;
+  if (nbw > 0) {
+    const int64_t o = tile_off(0);
+    load_k<D>(A, k_pool + o, lane);
+    load_v<D>(A, v_pool + o, lane);
   }
+  if (kEarlyRefill && nbw > 1) {
+    const int64_t o = tile_off(1);
+    load_k<D>(B, k_pool + o, lane);
+    load_v<D>(B, v_pool + o, lane);
+  }
+#pragma unroll
+  for (int k = 0; k < (QCH + 255) / 256; ++k)
+    if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
+  __syncthreads();
 
   WaveState<D, G> st;
 #pragma unroll
@@ -282,51 +334,63 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     for (int e = 0; e < EPL; ++e) st.acc[h][e] = 0.f;
   }
 
-  const int64_t tile_elems = (int64_t)16 * D;
-  const int64_t head_off = (int64_t)g * tile_elems;
-  const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
-  if (nbw > 0) {
-    KVRegs<D> A, B;
-    int bid = __builtin_amdgcn_readlane(my_bid, 0);
-    load_kv<D>(A, k_pool + bid * block_stride + head_off, v_pool + bid * block_stride + head_off,
-               lane);
-    for (int k = 0; k < nbw; k += 2) {
+  // Blocks k (in A) and k+1 (in B) per trip, buffer roles fixed so both stay
+  // in registers.
+  auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
+  for (int k = 0; k < nbw; k += 2) {
+    if constexpr (kEarlyRefill) {
+      // block k+2 goes into A (K after the scores, V after P.V), k+3 into B
+      const int64_t oa = k + 2 < nbw ? tile_off(k + 2) : 0;
+      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 2 < nbw) load_k<D>(A, k_pool + oa, lane);
+      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 2 < nbw) load_v<D>(A, v_pool + oa, lane);
+      if (k + 1 >= nbw) break;
+      const int64_t ob = k + 3 < nbw ? tile_off(k + 3) : 0;
+      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 3 < nbw) load_k<D>(B, k_pool + ob, lane);
+      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 3 < nbw) load_v<D>(B, v_pool + ob, lane);
+    } else {
+      // block k+1 goes into B before A is computed, k+2 into A before B
       if (k + 1 < nbw) {
-        bid = __builtin_amdgcn_readlane(my_bid, k + 1);
-        load_kv<D>(B, k_pool + bid * block_stride + head_off,
-                   v_pool + bid * block_stride + head_off, lane);
+        const int64_t o = tile_off(k + 1);
+        load_k<D>(B, k_pool + o, lane);
+        load_v<D>(B, v_pool + o, lane);
       }
-      attend_block<D, G>(A, qf, st, (b0 + wave + kWaves * k) * 16, ctx, scale_log2, s_p[wave],
-                         lane);
+      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], lane);
+      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave]);
       if (k + 1 >= nbw) break;
       if (k + 2 < nbw) {
-        bid = __builtin_amdgcn_readlane(my_bid, k + 2);
-        load_kv<D>(A, k_pool + bid * block_stride + head_off,
-                   v_pool + bid * block_stride + head_off, lane);
+        const int64_t o = tile_off(k + 2);
+        load_k<D>(A, k_pool + o, lane);
+        load_v<D>(A, v_pool + o, lane);
       }
-      attend_block<D, G>(B, qf, st, (b0 + wave + kWaves * (k + 1)) * 16, ctx, scale_log2,
-                         s_p[wave], lane);
+      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], lane);
+      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave]);
     }
   }
 
-  // Lane groups' weight sums -> wave totals.
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) st.l[h] += __shfl_xor(st.l[h], off);
-
+  // Lane groups' weight sums -> wave totals; then merge the 4 waves.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    float lw = st.l[h];
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * lane + e] = st.acc[h][e];
     if (lane == 0) {
       s_m[wave][h] = st.m[h];
-      s_l[wave][h] = st.l[h];
+      s_l[wave][h] = lw;
     }
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+  for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
     const int h = idx / D, e = idx - h * D;
     float M = -__builtin_huge_valf();
 #pragma unroll
@@ -457,14 +521,17 @@ DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t nu
                        int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens) {
   DecodePlan plan{};
   const int32_t max_blocks = (max_context_len + 15) / 16;
+  const int32_t units = num_decode_seqs * num_kv_heads > 0 ? num_decode_seqs * num_kv_heads : 1;
   int32_t pb;
   if (kv_partition_tokens > 0) {
     pb = kv_partition_tokens / 16;
+  } else if (units >= kResidentGroups && max_blocks <= kMaxPartitionBlocks) {
+    pb = max_blocks;  // enough (sequence, KV head) pairs to fill the GPU: no split, no merge
   } else {
-    const int32_t units = num_decode_seqs * num_kv_heads > 0 ? num_decode_seqs * num_kv_heads : 1;
-    const int32_t splits = (kTargetGroups + units - 1) / units;
-    pb = (max_blocks + splits - 1) / splits;
-    if (pb < kMinPartitionBlocks) pb = kMinPartitionBlocks;
+    // cut the longest context so that there are about kTargetItems work-groups
+    // if every context were that long; shorter ones get fewer partitions
+    const int32_t splits = (kTargetItems + units - 1) / units;
+    pb = std::max((max_blocks + splits - 1) / splits, kMinPartitionBlocks);
   }
   pb = (pb + kWaves - 1) / kWaves * kWaves;
   if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
