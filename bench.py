@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--partition", type=int, default=0,
                     help="force split-KV partition tokens (multiple of 64; 0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (5 times), the "
+                         "reference for scaling HBM traffic counters, and exit")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     return ap.parse_args()
 
@@ -59,6 +62,23 @@ def algorithmic_bytes_per_attention_launch(wl) -> int:
     qo = 2 * wl.num_decode_seqs * wl.num_q_heads * wl.head_dim * 2
     ids = int((-(-ctx // wl.block_size)).sum()) * 4
     return kv + qo + ids
+
+
+def measured_traffic(wl):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary of this workload, or None when there is none or the decode
+    kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"paged_decode_{wl.name}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = dict(line.split(": ", 1) for line in open(path) if ": " in line and not line.startswith(" "))
+    h = hashlib.sha256()
+    for f in ("paged_kv_decode_append_amd/csrc/decode.hip", "paged_kv_decode_append_amd/csrc/device_util.h"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(wl, layer_tensors_dev, budget_s: float):
@@ -98,13 +118,23 @@ def main():
         sys.exit(2)
 
     import torch
-    import workloads
-    import paged_kv_decode_append_amd as pkv
-    from paged_kv_decode_append_amd.step import Step
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
+
+    import workloads
+    import paged_kv_decode_append_amd as pkv
+    from paged_kv_decode_append_amd.step import Step
 
     make = workloads.WORKLOADS[args.workload]
     overrides = {k: v for k, v in (("layers", args.layers), ("batch", args.batch),
@@ -133,27 +163,28 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
-    # Per-launch duration of the attention (decode + merge) with HIP events
-    # on the launch stream, in a separate pass so events do not perturb the above.
+    # Per-launch duration of the attention (decode + merge [+ prefill]) with HIP
+    # events on the launch stream: in a separate pass (so events do not
+    # perturb the step timing above), each step appends every layer first and
+    # then launches the L attention steps back to back between two events.
     stream = torch.cuda.current_stream()
-    n_ev = min(args.steps, 20) * wl.num_layers
+    reps = min(args.steps, 20)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_ev)]
-    k = 0
-    for _ in range(min(args.steps, 20)):
+          for _ in range(reps)]
+    for r in range(reps):
         step.plan()
-        for c, t, o in zip(caches, layers, outs):
+        for c, t in zip(caches, layers):
             pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
-            ev[k][0].record(stream)
+        ev[r][0].record(stream)
+        for c, t, o in zip(caches, layers, outs):
             pkv.paged_attention_step(c, t["q"], o, step.block_tables, step.context_lens,
                                      step.query_start_loc, step.num_decode_seqs, step.scale,
                                      step.max_context_len, step.max_query_len,
                                      workspace=step.workspace,
                                      kv_partition_tokens=step.kv_partition_tokens)
-            ev[k][1].record(stream)
-            k += 1
+        ev[r][1].record(stream)
     torch.cuda.synchronize()
-    attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3 / wl.num_layers
 
     alg_bytes = algorithmic_bytes_per_attention_launch(wl)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
@@ -191,7 +222,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl),
             "kernel": "paged decode attention (+ split-KV merge when split)",
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
