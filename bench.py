@@ -4,16 +4,20 @@
 A step is one pass of the whole hot path over one batch: slot mapping once,
 then for every layer the KV append followed by paged attention (decode +
 split-KV merge, plus prefill chunks where the workload has them), all on one
-stream, inputs resident in HBM.  Prints ONE JSON line.
+stream, inputs resident in HBM.  By default each layer is one
+pkv_append_attention_step call (the decode tokens are appended inside the
+decode kernel); --separate runs pkv_kv_append + pkv_paged_attention_step.
+Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--separate]
 
 value      = decode tokens per second of the whole step (decode sequences x
              steps / wall time), wall time between synchronisations.
 roofline   = the dominant kernel (paged decode + its merge): algorithmic
-             bytes per launch (KV of every context, Q and O, block ids) over
-             the launch's average duration from HIP events around each
-             attention launch, against the 8 TB/s HBM peak.
+             bytes per launch (KV of every context, Q and O, block ids, and
+             the appended rows when fused) over the launch's average
+             duration from HIP events around back-to-back attention
+             launches, against the 8 TB/s HBM peak.
 cpu_baseline = the fp64 CPU oracle, timed on the host on a bounded sample of
              the same workload (a few layers of the step), scaled to a step.
 """
@@ -47,6 +51,8 @@ def parse():
     ap.add_argument("--ctx", type=int, default=0, help="override the context length (uniform / long_context)")
     ap.add_argument("--partition", type=int, default=0,
                     help="force split-KV partition tokens (multiple of 64; 0 = automatic)")
+    ap.add_argument("--separate", action="store_true",
+                    help="append and attention as two calls per layer (default: one fused call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (5 times), the "
@@ -55,13 +61,17 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes_per_attention_launch(wl) -> int:
-    """KV of every decode context + Q and O rows + block ids, one layer."""
-    ctx = wl.context_lens[: wl.num_decode_seqs].astype(np.int64)
+def algorithmic_bytes_per_attention_launch(wl, fused: bool) -> int:
+    """KV of every decode context + Q and O rows + block ids, one layer; when
+    the decode tokens are appended in the same kernel, + their K/V rows read
+    and written and their slots."""
+    B = wl.num_decode_seqs
+    ctx = wl.context_lens[:B].astype(np.int64)
     kv = int(ctx.sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
-    qo = 2 * wl.num_decode_seqs * wl.num_q_heads * wl.head_dim * 2
+    qo = 2 * B * wl.num_q_heads * wl.head_dim * 2
     ids = int((-(-ctx // wl.block_size)).sum()) * 4
-    return kv + qo + ids
+    app = (2 * 2 * B * wl.num_kv_heads * wl.head_dim * 2 + 8 * B) if fused else 0
+    return kv + qo + ids + app
 
 
 def measured_traffic(wl):
@@ -146,10 +156,12 @@ def main():
     step = Step.from_workload(wl, kv_partition_tokens=args.partition)
     torch.cuda.synchronize()
 
+    fused = not args.separate
+
     def run_step():
         step.plan()
         for c, t, o in zip(caches, layers, outs):
-            step.layer(c, t["q"], t["k_new"], t["v_new"], o)
+            step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=fused)
 
     for _ in range(args.warmup):
         run_step()
@@ -164,29 +176,34 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     # Per-launch duration of the attention (decode + merge [+ prefill]) with HIP
-    # events on the launch stream: in a separate pass (so events do not
-    # perturb the step timing above), each step appends every layer first and
-    # then launches the L attention steps back to back between two events.
+    # events on the launch stream, in a separate pass so that events do not
+    # perturb the step timing above: the L layers' attention calls run back
+    # to back between two events (fused: the whole step is those calls; when
+    # separate, each pass appends every layer first).
     stream = torch.cuda.current_stream()
     reps = min(args.steps, 20)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for r in range(reps):
         step.plan()
-        for c, t in zip(caches, layers):
-            pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
+        if not fused:
+            for c, t in zip(caches, layers):
+                pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
         ev[r][0].record(stream)
         for c, t, o in zip(caches, layers, outs):
-            pkv.paged_attention_step(c, t["q"], o, step.block_tables, step.context_lens,
-                                     step.query_start_loc, step.num_decode_seqs, step.scale,
-                                     step.max_context_len, step.max_query_len,
-                                     workspace=step.workspace,
-                                     kv_partition_tokens=step.kv_partition_tokens)
+            if fused:
+                step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=True)
+            else:
+                pkv.paged_attention_step(c, t["q"], o, step.block_tables, step.context_lens,
+                                         step.query_start_loc, step.num_decode_seqs, step.scale,
+                                         step.max_context_len, step.max_query_len,
+                                         workspace=step.workspace,
+                                         kv_partition_tokens=step.kv_partition_tokens)
         ev[r][1].record(stream)
     torch.cuda.synchronize()
     attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3 / wl.num_layers
 
-    alg_bytes = algorithmic_bytes_per_attention_launch(wl)
+    alg_bytes = algorithmic_bytes_per_attention_launch(wl, fused)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
     kv_bytes_step = wl.kv_read_bytes_per_layer(decode_only=True) * wl.num_layers
     result = {
@@ -215,6 +232,7 @@ def main():
             "max_context": wl.max_context_len,
             "pool_blocks_per_layer": wl.num_blocks,
             "parallelism": "single-gpu",
+            "append": "fused into the decode kernel" if fused else "separate kernel",
         },
         "roofline": {
             "bound": "hbm",
@@ -222,8 +240,10 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl),
-            "kernel": "paged decode attention (+ split-KV merge when split)",
+            "traffic": measured_traffic(wl) if fused else None,
+            "kernel": ("paged decode attention with the decode tokens' append fused in"
+                       if fused else "paged decode attention") +
+                      " (+ split-KV merge when split)",
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
         },

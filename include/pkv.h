@@ -23,6 +23,9 @@
  *   3. pkv_paged_attention_step -- every new query token attends its own
  *      context through the block table: decode sequences (one token each)
  *      over their whole context, prefill chunks causally.
+ * pkv_append_attention_step does 2 and 3 in one call with the same result,
+ * appending the decode tokens inside the decode kernel (one launch fewer
+ * per layer).
  *
  * Conventions shared by every entry point.
  *   - "device" pointers are GPU memory (hipMalloc / torch CUDA tensors),
@@ -200,6 +203,49 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_kv_append(cache, k_new, v_new, slot_mapping, num_tokens) followed by
+ * pkv_paged_attention_step(cache, q, out, ...) in one call, with the same
+ * result in the pools and in `out`.  A step's tokens are written into the
+ * cache before they are attended (deepconcepts.dev, "Continuous Batching Is
+ * Not a Bigger Batch", "What the scheduler does on one step"), and the many
+ * small GPU launches of a pass are a cost of their own, paid per pass
+ * (danielfleming.xyz, "Static batching", section "What changed").
+ *
+ * The decode tokens (rows 0 .. num_decode_seqs-1) are appended by the
+ * decode kernel itself: the work-group that reads the block holding
+ * position ctx_i - 1 takes the new row from k_new / v_new instead of the
+ * pool and writes it to slot_mapping[i] at its end.  Prefill tokens (rows
+ * num_decode_seqs .. num_tokens-1) are appended by the append kernel before
+ * the prefill kernel runs.
+ *
+ *   k_new, v_new   device fp16 [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping   device int64 [num_tokens]; as for pkv_kv_append.  The
+ *                  fused decode append assumes each decode token's slot is
+ *                  either negative (skipped: the attention then reads the
+ *                  pool's current row) or the slot that the block table
+ *                  gives position ctx_i - 1 (what pkv_slot_mapping writes;
+ *                  pkv_validate_step code 9); a slot elsewhere is written,
+ *                  but the attention does not see it.
+ *   num_tokens     rows of k_new / v_new / q (= qsl[num_seqs], or num_seqs
+ *                  when query_start_loc is NULL); >= num_decode_seqs
+ *   other arguments exactly as for pkv_paged_attention_step, with the same
+ *                  workspace size (pkv_attention_workspace_size).
+ * The rows of a sequence whose ctx_i < 1 are not written.
+ * Errors: PKV_ERR_INVALID_ARG (also: k_new, v_new or slot_mapping NULL,
+ * num_tokens inconsistent), PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
+ * PKV_ERR_HIP.
+ */
+int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping, int32_t num_tokens, const void* q,
+                              void* out, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_decode_seqs, int32_t num_q_heads, float scale,
+                              int32_t max_context_len, int32_t max_query_len,
+                              int32_t kv_partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Debug validator (host, synchronous, no GPU): checks on host copies of
  * the step's index arrays every device-content contract the hot path
  * assumes.  Returns PKV_OK, or PKV_ERR_CONTRACT with *bad_what set to one
@@ -214,6 +260,8 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
  *   6  a slot outside [0, num_blocks * block_size) (negative = skipped)
  *   7  two new tokens with the same non-negative slot
  *   8  max_context_len or max_query_len smaller than an actual length
+ *   9  a non-negative slot that is not the table's slot of its token's
+ *      position (ctx_i - n_i + k)
  */
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, const int32_t* query_start_loc,

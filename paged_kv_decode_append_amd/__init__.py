@@ -5,7 +5,7 @@ libpkv.so; torch supplies device memory and the stream.  The names follow
 the C ABI in include/pkv.h without the ``pkv_`` prefix:
 
     slot_mapping, kv_append, attention_workspace_size, paged_attention_step,
-    validate_step, status_string, last_hip_error, version
+    append_attention_step, validate_step, status_string, last_hip_error, version
 
 There is no fallback: importing this package without a built libpkv.so
 raises, and every call raises PkvError on a non-OK status.
@@ -30,7 +30,8 @@ PKV_ERR_CONTRACT = -5
 # every symbol include/pkv.h declares
 EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_hip_error", "pkv_slot_mapping", "pkv_kv_append",
-    "pkv_attention_workspace_size", "pkv_paged_attention_step", "pkv_validate_step",
+    "pkv_attention_workspace_size", "pkv_paged_attention_step", "pkv_append_attention_step",
+    "pkv_validate_step",
 )
 
 
@@ -73,6 +74,9 @@ def _load():
     lib.pkv_paged_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, i32, i32,
                                              i32, ctypes.c_float, i32, i32, i32, P,
                                              ctypes.c_size_t, P]
+    lib.pkv_append_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, P, i32,
+                                              P, P, i32, i32, i32, ctypes.c_float, i32, i32, i32,
+                                              P, ctypes.c_size_t, P]
     lib.pkv_validate_step.argtypes = [P, i32, P, P, i32, i32, i64, i32, P, i32, i32, i32,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     for name in EXPORTED:
@@ -227,6 +231,41 @@ def paged_attention_step(cache: KVCache, q, out, block_tables, context_lens, que
         q.shape[1], float(scale), int(max_context_len), int(max_query_len),
         int(kv_partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_paged_attention_step")
+    return out
+
+
+def append_attention_step(cache: KVCache, k_new, v_new, slot_mapping_t, q, out, block_tables,
+                          context_lens, query_start_loc, num_decode_seqs: int, scale: float,
+                          max_context_len: int, max_query_len: int, workspace=None,
+                          kv_partition_tokens: int = 0, stream=None):
+    """pkv_append_attention_step: kv_append then paged_attention_step in one
+    call, the decode tokens appended inside the decode kernel."""
+    import torch
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (q, "q"), (out, "out")):
+        _need(t, torch.float16, name)
+    _need(slot_mapping_t, torch.int64, "slot_mapping")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if query_start_loc is not None:
+        _need(query_start_loc, torch.int32, "query_start_loc")
+    T = k_new.shape[0]
+    if v_new.shape != k_new.shape or k_new.shape[1:] != (cache.num_kv_heads, cache.head_dim):
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    if out.shape != q.shape or q.dim() != 3 or q.shape[0] != T or q.shape[2] != cache.head_dim:
+        raise ValueError("q and out must be [T, num_q_heads, head_dim]")
+    if slot_mapping_t.numel() < T:
+        raise ValueError("slot_mapping shorter than the token count")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    rc = lib.pkv_append_attention_step(
+        ctypes.byref(cache._c), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping_t), T, _ptr(q),
+        _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(query_start_loc), context_lens.shape[0], num_decode_seqs, q.shape[1], float(scale),
+        int(max_context_len), int(max_query_len), int(kv_partition_tokens), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    _check(rc, "pkv_append_attention_step")
     return out
 
 

@@ -129,20 +129,31 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
   return PKV_OK;
 }
 
-int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out,
-                             const int32_t* block_tables, int32_t max_blocks_per_seq,
-                             const int32_t* context_lens, const int32_t* query_start_loc,
-                             int32_t num_seqs, int32_t num_decode_seqs,
-                             int32_t num_q_heads, float scale,
-                             int32_t max_context_len, int32_t max_query_len,
-                             int32_t kv_partition_tokens,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Attention of one layer; with k_new non-null the new tokens' append is done
+// here too: the decode tokens' inside the decode kernel, the prefill tokens'
+// by the append kernel ahead of the prefill kernel.
+int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int32_t num_tokens, const void* q, void* out,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* context_lens, const int32_t* query_start_loc,
+                   int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_heads, float scale,
+                   int32_t max_context_len, int32_t max_query_len, int32_t kv_partition_tokens,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, cache->num_kv_heads,
                         cache->head_dim, max_context_len, max_query_len, kv_partition_tokens);
   if (rc != PKV_OK) return rc;
   if (!std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
+  const bool fused = k_new != nullptr;
+  if (fused) {
+    if (!v_new || !slot_mapping || num_tokens < num_decode_seqs) return PKV_ERR_INVALID_ARG;
+    if (!query_start_loc && num_tokens != num_seqs) return PKV_ERR_INVALID_ARG;
+  }
   if (num_seqs == 0) return PKV_OK;
   if (!q || !out || !block_tables || !context_lens || max_blocks_per_seq <= 0)
     return PKV_ERR_INVALID_ARG;
@@ -160,16 +171,61 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused && num_tokens > num_decode_seqs) {
+    // rows of the prefill chunks follow the decode rows
+    const size_t row_bytes = (size_t)cache->num_kv_heads * cache->head_dim * 2;
+    rc = from_hip(pkv::launch_kv_append(
+        cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, cache->head_dim,
+        static_cast<const char*>(k_new) + (size_t)num_decode_seqs * row_bytes,
+        static_cast<const char*>(v_new) + (size_t)num_decode_seqs * row_bytes,
+        slot_mapping + num_decode_seqs, num_tokens - num_decode_seqs, s));
+    if (rc != PKV_OK) return rc;
+  }
+  const pkv::DecodeAppend app{k_new, v_new, fused ? slot_mapping : nullptr};
   rc = from_hip(pkv::launch_paged_decode(
       q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
       cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
-      plan, out, workspace, s));
+      plan, app, out, workspace, s));
   if (rc != PKV_OK) return rc;
   return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, cache->num_blocks,
                                       cache->num_kv_heads, num_q_heads, cache->head_dim,
                                       block_tables, max_blocks_per_seq, context_lens,
                                       query_start_loc, num_decode_seqs, num_prefill,
                                       max_query_len, scale, pplan, out, prefill_ws, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t num_decode_seqs,
+                             int32_t num_q_heads, float scale,
+                             int32_t max_context_len, int32_t max_query_len,
+                             int32_t kv_partition_tokens,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_step(cache, nullptr, nullptr, nullptr, 0, q, out, block_tables,
+                        max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
+                        num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
+                        kv_partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+                              const int64_t* slot_mapping, int32_t num_tokens, const void* q,
+                              void* out, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_decode_seqs, int32_t num_q_heads, float scale,
+                              int32_t max_context_len, int32_t max_query_len,
+                              int32_t kv_partition_tokens, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!k_new) return PKV_ERR_INVALID_ARG;
+  return attention_step(cache, k_new, v_new, slot_mapping, num_tokens, q, out, block_tables,
+                        max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
+                        num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
+                        kv_partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -215,6 +271,18 @@ int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
       if (s < 0) continue;
       if (s >= num_blocks * block_size) return fail(6, t);
       if (!seen.insert(s).second) return fail(7, t);
+    }
+    // every non-negative slot is the table's slot of its token's position
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t first = query_start_loc ? query_start_loc[i] : i;
+      const int32_t n = query_start_loc ? query_start_loc[i + 1] - first : 1;
+      for (int32_t k = 0; k < n; ++k) {
+        const int64_t s = slot_mapping[first + k];
+        if (s < 0) continue;
+        const int64_t p = (int64_t)context_lens[i] - n + k;
+        const int64_t b = block_tables[(int64_t)i * max_blocks_per_seq + p / block_size];
+        if (s != b * block_size + p % block_size) return fail(9, first + k);
+      }
     }
   }
   return PKV_OK;

@@ -134,17 +134,30 @@ __device__ __forceinline__ void pv_dword(float (&acc)[G][2], const uint32_t (&pr
 // tok0 = logical position of the block's first token.
 // qs = the segment's G query rows in LDS ([G][D] fp16); each lane reads its
 // 16-value fragments per block instead of holding them in registers.
+// knew: when not null, the K row appended in this step for position ctx - 1
+// ([D] fp16 in LDS); it replaces that row of the block holding ctx - 1.
 template <int D, int G>
-__device__ __forceinline__ void block_scores(const KVRegs<D>& r, const uint16_t* qs,
+__device__ __forceinline__ void block_scores(KVRegs<D>& r, const uint16_t* qs,
                                              WaveState<D, G>& st, int tok0, int ctx,
                                              float scale_log2, uint32_t* __restrict__ p_lds,
-                                             int lane) {
+                                             const uint16_t* knew, int lane) {
   constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
   constexpr int GP = (G + 3) & ~3;
   const int tl = lane / LPT, c = lane % LPT;
   const bool tail = tok0 + 16 > ctx;
   const float kNegInf = -__builtin_huge_valf();
   asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
+  if (knew != nullptr && tok0 + 16 >= ctx) {
+    const int row = ctx - 1 - tok0;
+    const uint4 n0 = *reinterpret_cast<const uint4*>(knew + 8 * c);
+    const uint4 n1 = *reinterpret_cast<const uint4*>(knew + 8 * (c + LPT));
+#pragma unroll
+    for (int s = 0; s < SPB; ++s)
+      if (tl + TPS * s == row) {
+        r.k[s][0] = n0;
+        r.k[s][1] = n1;
+      }
+  }
 
   // Scores of this lane group's SPB tokens (tl + TPS*s) for every head.
   float x[SPB][G];
@@ -211,12 +224,23 @@ __device__ __forceinline__ void block_scores(const KVRegs<D>& r, const uint16_t*
 }
 
 // Second half: P.V from the V registers and the weights in LDS.  Rows of
-// positions >= ctx are zeroed first (select), so stale slots never leak.
+// positions >= ctx are zeroed first (select), so stale slots never leak;
+// vnew, when not null, is the V row appended for position ctx - 1 (LDS).
 template <int D, int G>
 __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int tok0, int ctx,
-                                         const uint32_t* __restrict__ p_lds) {
+                                         const uint32_t* __restrict__ p_lds,
+                                         const uint16_t* vnew, int lane) {
   constexpr int TPS = KVRegs<D>::TPS;
   constexpr int GP = (G + 3) & ~3;
+  if (vnew != nullptr && tok0 + 16 >= ctx) {
+    // one bit per token row, tested with constant t: keeps r.v in registers
+    const uint32_t hit = 1u << (ctx - 1 - tok0);
+    const typename VFrag<D>::T nv =
+        *reinterpret_cast<const typename VFrag<D>::T*>(vnew + (D / 64) * lane);
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      if (hit & (1u << t)) r.v[t] = nv;
+  }
   if (tok0 + 16 > ctx) {
 #pragma unroll
     for (int t = 0; t < 16; ++t)
@@ -252,39 +276,54 @@ __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int 
 }
 
 
-template <int D, int G>
+// APPEND: the step's decode tokens are appended by this kernel (fused
+// append): k_new / v_new row i (one token of sequence i, [Hkv][D]) belongs
+// at position ctx_i - 1.  The work-group whose partition holds that position
+// stages the row in LDS, uses it in place of the pool's old row when
+// slot_mapping[i] is the table's slot of ctx_i - 1, and writes it to
+// slot_mapping[i] at the end (nothing when the slot is negative or beyond
+// the pool), so the result equals an append followed by the attention.
+template <int D, int G, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ k_pool,
+    uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
     const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
   constexpr int LPT = D / 16, EPL = D / 64, GP = (G + 3) & ~3;
   // d = 128: two blocks (16 KiB) in flight per wave by refilling a buffer as
   // soon as each half is consumed; d = 256: one block is already 16 KiB, and
   // the plain two-buffer scheme keeps registers under 256 (2 waves per SIMD).
   constexpr bool kEarlyRefill = D == 128;
+  constexpr int RCH = D / 8;  // 16-byte chunks of one appended row
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
   __shared__ uint32_t s_p[kWaves][8 * GP];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 2 * D : 8];  // K row, V row
 
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
-  // A length beyond the table row or the planned partitions breaks the
-  // caller contract; clamp so that it can only give wrong numbers.
-  const int ctx = min(context_lens[i], ctx_clamp);
-  const int nblk = (ctx + 15) >> 4;
-  const int b0 = part * partition_blocks;
-  if (ctx <= 0 || b0 >= nblk) return;  // uniform over the work-group
-  const int b1 = min(b0 + partition_blocks, nblk);
-  const int nparts = (nblk + partition_blocks - 1) / partition_blocks;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b0 = part * partition_blocks;
+  const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
 
-  // Query rows of the G heads -> LDS (issued first; used after the barrier).
+  // Everything that does not depend on the context length is requested
+  // first, so that the length, the block ids, the query rows and the
+  // appended rows arrive together: block ids of this wave's blocks
+  // b0 + wave + kWaves*k (one per lane, k < the partition's share; entries
+  // past the context are never used) ...
+  uint32_t raw_bid = 0;
+  {
+    const int e = b0 + wave + kWaves * lane;
+    if (wave + kWaves * lane < partition_blocks && e < max_blocks_per_seq)
+      raw_bid = (uint32_t)bt_row[e];
+  }
+  // ... the query rows of the G heads (to LDS after the first K/V loads) ...
   const uint4* qsrc =
       reinterpret_cast<const uint4*>(q + ((int64_t)i * num_q_heads + (int64_t)g * G) * D);
   constexpr int QCH = G * D / 8;
@@ -292,16 +331,31 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) qstage[k] = qsrc[tid + 256 * k];
-
-  // Block ids of this wave's blocks b0 + wave + kWaves*k, one per lane,
-  // clamped into the pool.
-  const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;
-  const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
-  int my_bid = 0;
-  if (lane < nbw) {
-    const uint32_t b = (uint32_t)bt_row[b0 + wave + kWaves * lane];
-    my_bid = (int)(b < (uint64_t)num_blocks ? b : (uint32_t)(num_blocks - 1));
+  // ... and the appended rows with their slot.
+  uint4 nstage{};
+  int64_t slot = -1;
+  if constexpr (APPEND) {
+    slot = slot_mapping[i];
+    const int64_t row = ((int64_t)i * num_kv_heads + g) * D;
+    if (tid < RCH)
+      nstage = reinterpret_cast<const uint4*>(k_new + row)[tid];
+    else if (tid >= 64 && tid < 64 + RCH)
+      nstage = reinterpret_cast<const uint4*>(v_new + row)[tid - 64];
   }
+
+  // A length beyond the table row or the planned partitions breaks the
+  // caller contract; clamp so that it can only give wrong numbers.
+  const int ctx = min(context_lens[i], ctx_clamp);
+  const int nblk = (ctx + 15) >> 4;
+  if (ctx <= 0 || b0 >= nblk) return;  // uniform over the work-group
+  const int b1 = min(b0 + partition_blocks, nblk);
+  const int nparts = (nblk + partition_blocks - 1) / partition_blocks;
+
+  // Block ids clamped into the pool.
+  const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;
+  const int my_bid =
+      lane < nbw ? (int)(raw_bid < (uint64_t)num_blocks ? raw_bid : (uint32_t)(num_blocks - 1))
+                 : 0;
   const int64_t tile_elems = (int64_t)16 * D;
   const int64_t head_off = (int64_t)g * tile_elems;
   const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
@@ -323,7 +377,30 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
+  if constexpr (APPEND) {
+    if (tid < RCH)
+      reinterpret_cast<uint4*>(s_new)[tid] = nstage;
+    else if (tid >= 64 && tid < 64 + RCH)
+      reinterpret_cast<uint4*>(s_new + D)[tid - 64] = nstage;
+  }
   __syncthreads();
+
+  // The appended token sits in block nblk - 1; this partition holds it when
+  // nblk <= b1, and the wave that reads that block substitutes the rows.
+  const bool owner = APPEND && nblk <= b1;
+  const uint16_t* knew = nullptr;
+  const uint16_t* vnew = nullptr;
+  if constexpr (APPEND) {
+    const int kl = nblk - 1 - b0 - wave;  // multiple of kWaves when this wave reads it
+    if (owner && kl >= 0 && kl % kWaves == 0 && slot >= 0) {
+      const uint32_t raw_last = (uint32_t)__builtin_amdgcn_readlane((int)raw_bid, kl / kWaves);
+      if (raw_last < (uint64_t)num_blocks &&
+          slot == (int64_t)raw_last * 16 + ((ctx - 1) & 15)) {
+        knew = s_new;
+        vnew = s_new + D;
+      }
+    }
+  }
 
   WaveState<D, G> st;
 #pragma unroll
@@ -341,18 +418,18 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     if constexpr (kEarlyRefill) {
       // block k+2 goes into A (K after the scores, V after P.V), k+3 into B
       const int64_t oa = k + 2 < nbw ? tile_off(k + 2) : 0;
-      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], lane);
+      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
       __builtin_amdgcn_sched_barrier(0);
       if (k + 2 < nbw) load_k<D>(A, k_pool + oa, lane);
-      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave]);
+      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
       __builtin_amdgcn_sched_barrier(0);
       if (k + 2 < nbw) load_v<D>(A, v_pool + oa, lane);
       if (k + 1 >= nbw) break;
       const int64_t ob = k + 3 < nbw ? tile_off(k + 3) : 0;
-      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], lane);
+      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], knew, lane);
       __builtin_amdgcn_sched_barrier(0);
       if (k + 3 < nbw) load_k<D>(B, k_pool + ob, lane);
-      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave]);
+      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave], vnew, lane);
       __builtin_amdgcn_sched_barrier(0);
       if (k + 3 < nbw) load_v<D>(B, v_pool + ob, lane);
     } else {
@@ -362,16 +439,16 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
         load_k<D>(B, k_pool + o, lane);
         load_v<D>(B, v_pool + o, lane);
       }
-      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], lane);
-      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave]);
+      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
+      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
       if (k + 1 >= nbw) break;
       if (k + 2 < nbw) {
         const int64_t o = tile_off(k + 2);
         load_k<D>(A, k_pool + o, lane);
         load_v<D>(A, v_pool + o, lane);
       }
-      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], lane);
-      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave]);
+      block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], knew, lane);
+      block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave], vnew, lane);
     }
   }
 
@@ -414,6 +491,19 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
         part_ml[pidx * 2] = M;
         part_ml[pidx * 2 + 1] = L;
       }
+    }
+  }
+
+  // The appended rows go to their slot (only this work-group reads the
+  // block that holds them, and it is done with it).
+  if constexpr (APPEND) {
+    if (owner && slot >= 0 && (slot >> 4) < num_blocks) {
+      const int64_t dst = (((slot >> 4) * num_kv_heads + g) * 16 + (slot & 15)) * D;
+      if (tid < RCH)
+        reinterpret_cast<uint4*>(k_pool + dst)[tid] = reinterpret_cast<const uint4*>(s_new)[tid];
+      else if (tid >= 64 && tid < 64 + RCH)
+        reinterpret_cast<uint4*>(v_pool + dst)[tid - 64] =
+            reinterpret_cast<const uint4*>(s_new + D)[tid - 64];
     }
   }
 }
@@ -467,13 +557,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
   }
 }
 
-template <int D, int G>
-hipError_t launch_decode_dg(const void* q, const void* k_pool, const void* v_pool,
-                            int64_t num_blocks, int32_t num_kv_heads,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            const int32_t* context_lens, int32_t num_decode_seqs, float scale,
-                            const DecodePlan& plan, void* out, void* workspace,
-                            hipStream_t stream) {
+template <int D, int G, bool APPEND>
+hipError_t launch_decode_dga(const void* q, void* k_pool, void* v_pool, int64_t num_blocks,
+                             int32_t num_kv_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                             const DecodeAppend& app, void* out, void* workspace,
+                             hipStream_t stream) {
   const int32_t num_q_heads = num_kv_heads * G;
   const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
                                             (int64_t)plan.max_parts * plan.partition_blocks * 16);
@@ -482,13 +572,14 @@ hipError_t launch_decode_dg(const void* q, const void* k_pool, const void* v_poo
   float* part_ml =
       part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((paged_decode_kernel<D, G>),
+  hipLaunchKernelGGL((paged_decode_kernel<D, G, APPEND>),
                      dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
-                     stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool),
-                     num_blocks, num_kv_heads, block_tables, max_blocks_per_seq, context_lens,
-                     ctx_clamp, plan.partition_blocks, plan.max_parts, scale * kLog2e,
-                     static_cast<uint16_t*>(out), part_o, part_ml);
+                     stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(k_pool),
+                     static_cast<uint16_t*>(v_pool), num_blocks, num_kv_heads, block_tables,
+                     max_blocks_per_seq, context_lens, ctx_clamp, plan.partition_blocks,
+                     plan.max_parts, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
+                     part_ml, static_cast<const uint16_t*>(app.k_new),
+                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
   const int32_t rows = num_decode_seqs * num_q_heads;
@@ -499,14 +590,20 @@ hipError_t launch_decode_dg(const void* q, const void* k_pool, const void* v_poo
 }
 
 template <int D>
-hipError_t launch_decode_d(int32_t group, const void* q, const void* k_pool, const void* v_pool,
+hipError_t launch_decode_d(int32_t group, const void* q, void* k_pool, void* v_pool,
                            int64_t num_blocks, int32_t num_kv_heads, const int32_t* bt,
                            int32_t maxblk, const int32_t* ctx, int32_t nseq, float scale,
-                           const DecodePlan& plan, void* out, void* ws, hipStream_t stream) {
-#define PKV_CASE(GG)                                                                          \
-  case GG:                                                                                   \
-    return launch_decode_dg<D, GG>(q, k_pool, v_pool, num_blocks, num_kv_heads, bt, maxblk, \
-                                   ctx, nseq, scale, plan, out, ws, stream);
+                           const DecodePlan& plan, const DecodeAppend& app, void* out, void* ws,
+                           hipStream_t stream) {
+  const bool fused = app.k_new != nullptr;
+#define PKV_CASE(GG)                                                                         \
+  case GG:                                                                                  \
+    return fused ? launch_decode_dga<D, GG, true>(q, k_pool, v_pool, num_blocks,            \
+                                                  num_kv_heads, bt, maxblk, ctx, nseq,      \
+                                                  scale, plan, app, out, ws, stream)        \
+                 : launch_decode_dga<D, GG, false>(q, k_pool, v_pool, num_blocks,           \
+                                                   num_kv_heads, bt, maxblk, ctx, nseq,     \
+                                                   scale, plan, app, out, ws, stream);
   switch (group) {
     PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
     PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
@@ -544,22 +641,22 @@ DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t nu
   return plan;
 }
 
-hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                               int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                               int32_t head_dim, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* context_lens,
-                               int32_t num_decode_seqs, float scale, const DecodePlan& plan,
-                               void* out, void* workspace, hipStream_t stream) {
+hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_t num_blocks,
+                               int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_decode_seqs, float scale,
+                               const DecodePlan& plan, const DecodeAppend& app, void* out,
+                               void* workspace, hipStream_t stream) {
   if (num_decode_seqs == 0) return hipSuccess;
   const int32_t group = num_q_heads / num_kv_heads;
   if (head_dim == 128)
     return launch_decode_d<128>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                 block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
-                                scale, plan, out, workspace, stream);
+                                scale, plan, app, out, workspace, stream);
   if (head_dim == 256)
     return launch_decode_d<256>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                 block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
-                                scale, plan, out, workspace, stream);
+                                scale, plan, app, out, workspace, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,12 +29,21 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t num_q_heads,
                        int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens);
 
-hipError_t launch_paged_decode(const void* q, const void* k_pool, const void* v_pool,
-                               int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                               int32_t head_dim, const int32_t* block_tables,
-                               int32_t max_blocks_per_seq, const int32_t* context_lens,
-                               int32_t num_decode_seqs, float scale, const DecodePlan& plan,
-                               void* out, void* workspace, hipStream_t stream);
+// The decode tokens' rows to append inside the decode kernel (row i of
+// k_new / v_new [num_decode_seqs][Hkv][d] to slot_mapping[i]); all null for
+// attention only.
+struct DecodeAppend {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+};
+
+hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_t num_blocks,
+                               int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_decode_seqs, float scale,
+                               const DecodePlan& plan, const DecodeAppend& app, void* out,
+                               void* workspace, hipStream_t stream);
 
 // Split-KV plan of the prefill chunks: each 64-row query tile is cut into
 // `splits` ranges of context tiles, merged by log-sum-exp when splits > 1.

@@ -7,8 +7,10 @@ metadata shared by every layer, while the pools are per layer.  Per step:
 
     pkv_slot_mapping                      (once)
     for every layer:
-        pkv_kv_append                     (this layer's new K/V into its pool)
-        pkv_paged_attention_step          (decode + merge [+ prefill chunks])
+        pkv_append_attention_step         (this layer's new K/V into its pool,
+                                           decode + merge [+ prefill chunks])
+    or, with fused=False, the two halves as separate calls:
+        pkv_kv_append ; pkv_paged_attention_step
 
 all enqueued on one stream; append precedes attention within a layer.
 """
@@ -16,8 +18,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (KVCache, attention_workspace_size, kv_append, paged_attention_step,
-               slot_mapping)
+from . import (KVCache, append_attention_step, attention_workspace_size, kv_append,
+               paged_attention_step, slot_mapping)
 
 
 class Step:
@@ -60,8 +62,14 @@ class Step:
         slot_mapping(self.block_tables, self.context_lens, self.query_start_loc, self.num_tokens,
                      self.slot_mapping, stream=stream)
 
-    def layer(self, cache: KVCache, q, k_new, v_new, out, stream=None):
-        """Append this layer's new K/V, then attend."""
+    def layer(self, cache: KVCache, q, k_new, v_new, out, stream=None, fused: bool = True):
+        """Append this layer's new K/V, then attend (one call when fused)."""
+        if fused:
+            return append_attention_step(
+                cache, k_new, v_new, self.slot_mapping, q, out, self.block_tables,
+                self.context_lens, self.query_start_loc, self.num_decode_seqs, self.scale,
+                self.max_context_len, self.max_query_len, workspace=self.workspace,
+                kv_partition_tokens=self.kv_partition_tokens, stream=stream)
         kv_append(cache, k_new, v_new, self.slot_mapping, stream=stream)
         paged_attention_step(cache, q, out, self.block_tables, self.context_lens,
                              self.query_start_loc, self.num_decode_seqs, self.scale,

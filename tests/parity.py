@@ -45,11 +45,18 @@ def all_position_slots(wl, tables=None):
     return oracle.slot_mapping(tables, wl.context_lens, qsl, wl.block_size)
 
 
-def poison_stale(wl, tensors, poison_table_tail=True):
+def poison_stale(wl, tensors, poison_table_tail=True, poison_new=True):
     """NaN (0x7E00) in every pool slot outside the sequences' contexts, and
-    point table entries past ceil(ctx/16) at a poisoned free block."""
+    point table entries past ceil(ctx/16) at a poisoned free block.  With
+    poison_new, the slots the step's new tokens are appended to hold NaN too
+    before the step: an attention that read one of them before (or instead
+    of) its append would give NaN."""
     live = np.zeros(wl.num_blocks * wl.block_size, bool)
     live[all_position_slots(wl)] = True
+    if poison_new:
+        qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None
+        new_slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, wl.block_size)
+        live[new_slots[new_slots >= 0]] = False
     dead = torch.from_numpy(np.nonzero(~live)[0]).to(tensors["k_pool"].device)
     for name in ("k_pool", "v_pool"):
         view = tensors[name].transpose(1, 2)          # [NB, 16, Hkv, d] view of the pool
@@ -65,8 +72,11 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison: bool = True,
-                        seq_subset=None, tensors=None, row_samples=None):
+                        seq_subset=None, tensors=None, row_samples=None, fused: bool = True):
     """One layer of one step on the GPU, checked against the oracle.
+
+    fused: the layer runs as pkv_append_attention_step (the benchmark's
+    path), else as pkv_kv_append followed by pkv_paged_attention_step.
 
     Checks: slot mapping bit-exact; whole pools after the append bit-exact
     (canaries and NaN poison included); attention within tolerance for the
@@ -85,7 +95,7 @@ def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison
     step.plan()
     cache = pkv.KVCache(t["k_pool"], t["v_pool"])
     out = torch.full_like(t["q"], float("nan"))
-    step.layer(cache, t["q"], t["k_new"], t["v_new"], out)
+    step.layer(cache, t["q"], t["k_new"], t["v_new"], out, fused=fused)
     torch.cuda.synchronize()
 
     qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None

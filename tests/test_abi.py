@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import paged_kv_decode_append_amd as pkv
+import oracle
 import workloads
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
@@ -85,6 +86,27 @@ def test_attention_step_argument_errors():
     assert _step(c, nseq=0, ndec=0) == pkv.PKV_OK         # empty step: nothing to do
 
 
+def _fused(cache, kn=FAKE, vn=FAKE, slots=FAKE, T=4, q=FAKE, out=FAKE, bt=FAKE, maxblk=64,
+           ctx=FAKE, qsl=None, nseq=4, ndec=4, hq=12, scale=0.1, mcl=1024, mql=1, part=0, ws=None,
+           wsb=0):
+    return pkv.lib.pkv_append_attention_step(ctypes.byref(cache), kn, vn, slots, T, q, out, bt,
+                                             maxblk, ctx, qsl, nseq, ndec, hq, scale, mcl, mql,
+                                             part, ws, wsb, None)
+
+
+def test_fused_step_argument_errors():
+    c = _cache()
+    assert _fused(c, kn=None) == -1
+    assert _fused(c, vn=None) == -1
+    assert _fused(c, slots=None) == -1
+    assert _fused(c, T=3) == -1                          # fewer rows than decode sequences
+    assert _fused(c, T=5) == -1                          # no query_start_loc: T must equal B
+    assert _fused(c, q=None) == -1
+    assert _fused(c, hq=18) == -2
+    assert _fused(c, mcl=4096, maxblk=256) == pkv.PKV_ERR_WORKSPACE
+    assert _fused(c, nseq=0, ndec=0, T=0) == pkv.PKV_OK
+
+
 def test_workspace_size_is_host_only_and_monotone():
     small = pkv.attention_workspace_size(4, 4, 12, 2, 128, 1024, 1)
     big = pkv.attention_workspace_size(4, 4, 12, 2, 128, 65536, 1)
@@ -125,3 +147,9 @@ def test_validator_reports_each_violation():
     assert v(slots=np.array([0, 5, wl.num_blocks * 16, 7], np.int64)) == (6, 2)
     assert v(slots=np.array([0, 5, -1, 5], np.int64)) == (7, 3)
     assert v(mcl=100) == (8, 2)                          # ctx 256 > 100
+    good = oracle.slot_mapping(bt, ctx, None, 16)
+    assert v(slots=good) == (0, -1)
+    pad = good.copy(); pad[2] = -1
+    assert v(slots=pad) == (0, -1)                       # a skipped token is fine
+    moved = good.copy(); moved[2] = wl.free_blocks[0] * 16  # a free slot, not its position's
+    assert v(slots=moved) == (9, 2)

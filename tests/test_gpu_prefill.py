@@ -13,13 +13,15 @@ def _report(name, errs):
     print(f"[parity] {name}: max_abs={errs[0]:.2e} norm_rel={errs[1]:.2e}", flush=True)
 
 
-def test_tiny_chunks_across_block_edges():
+@pytest.mark.parametrize("fused", [pytest.param(True, id="fused"),
+                                   pytest.param(False, id="separate")])
+def test_tiny_chunks_across_block_edges(fused):
     # decode sequences first, then chunks of 1..8 rows whose contexts cross 16/32
     ctx = [15, 16, 17, 31, 32, 33, 40, 16, 17, 33, 8]
     new = [1, 1, 1, 1, 1, 1, 8, 8, 3, 5, 8]
     wl = workloads.custom("tiny_chunks", ctx, new, 6, 12, 2, 128, seed=31)
-    _, _, errs = run_layer_and_check(wl)
-    _report("tiny chunks", errs)
+    _, _, errs = run_layer_and_check(wl, fused=fused)
+    _report(f"tiny chunks fused={fused}", errs)
 
 
 @pytest.mark.parametrize("d,hq,hkv", [(128, 12, 2), (128, 8, 8), (128, 16, 2), (256, 16, 4),
