@@ -40,10 +40,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRows = 64;    // query rows per work-group (16 per wave)
-constexpr int64_t kResidentGroups = 512;  // 256 CUs x 2 work-groups resident per CU
+constexpr int64_t kCUs = 256;
+// work-groups resident per CU (the kernel's occupancy: 3 or 2 waves per SIMD)
+constexpr int64_t kGroupsPerCU128 = 3;
+constexpr int64_t kGroupsPerCU256 = 2;
 constexpr uint32_t kXcds = 8;
 constexpr int64_t kMaxPrefillSplits = 16;
-constexpr int kLdsPad = 8;   // fp16 padding per LDS row (bank spread)
+constexpr float kRescaleSlack = 8.f;  // lazy max (base 2): rescale only past m + 8
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, const f32x4& c) {
@@ -56,9 +59,13 @@ struct PrefillShape {
   static constexpr int NT = KT / 16;             // 16-token sub-tiles
   static constexpr int KC = D / 32;              // 32-wide d chunks (S^T reduction)
   static constexpr int DT = D / 16;              // 16-row d tiles of O^T
-  static constexpr int KSTRIDE = D + kLdsPad;    // K tile row stride (fp16)
-  static constexpr int VSTRIDE = KT + kLdsPad;   // V^T row stride (fp16)
+  // K rows: 16-byte fragment reads by 8 lanes of 8 consecutive rows touch
+  // all 32 banks once with a row stride of 4 (mod 32) dwords; V^T rows:
+  // 8-byte reads by 16 lanes of 16 consecutive rows need 2 (mod 32).
+  static constexpr int KSTRIDE = D + 8;          // K tile row stride (fp16)
+  static constexpr int VSTRIDE = KT + 4;         // V^T row stride (fp16)
   static constexpr int LDS_BYTES = (KT * KSTRIDE + D * VSTRIDE) * 2;
+  static constexpr int kIdTiles = 64;            // tiles whose block ids are staged in LDS
 };
 
 // One thread's share of a K/V tile in flight: 4 K chunks of 16 bytes, and
@@ -68,8 +75,13 @@ struct TileRegs {
   uint4 v[4];
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(
+// HPW query heads of one KV group per wave (its 16 rows of each): every K
+// and V^T fragment read from LDS feeds HPW MFMAs.  Measured on MI355X, HPW = 2
+// needs ~350 registers (one wave per SIMD) and runs slower than HPW = 1 at
+// three waves per SIMD, whose waves hide each other's MFMA, LDS and exp
+// latencies; only HPW = 1 is launched.
+template <int D, int HPW>
+__global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGroupsPerCU256) : 1) void prefill_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
     int32_t num_q_heads, const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
@@ -80,12 +92,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   constexpr int KT = S::KT, NT = S::NT, KC = S::KC, DT = S::DT;
   static_assert(KT * (D / 8) == 4 * 256 && (KT / 4) * (D / 8) == 256, "tile split over 256 threads");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_BYTES / 2];
+  __shared__ int64_t s_tile_base[S::kIdTiles * (KT / 16)];  // pool offsets of staged blocks
   uint16_t* k_lds = lds;                         // [KT][KSTRIDE]
   uint16_t* vt_lds = lds + KT * S::KSTRIDE;      // [D][VSTRIDE]
 
   const int i = first_seq + blockIdx.z;
-  const int h = blockIdx.y;
-  const int g = h / (num_q_heads / num_kv_heads);
+  const int h0 = blockIdx.y * HPW;               // heads h0 .. h0 + HPW - 1, one KV group
+  const int g = h0 / (num_q_heads / num_kv_heads);
   const int split = blockIdx.x % num_splits;
   const int tile_row0 = (blockIdx.x / num_splits) * kRows;  // x past the last tile: exits below
   const int row_base = query_start_loc[i];
@@ -107,35 +120,51 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   const int my_row = row_valid ? my_row_raw : n - 1;
   const int my_pos = p0 + my_row;
 
-  // Q^T fragments: B operand, lane = query row lrow, 8 d values per 32-wide chunk.
-  f16x8 qb[KC];
-  const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + h) * D;
+  // Q^T fragments: B operands, lane = query row lrow, 8 d values per 32-wide chunk.
+  f16x8 qb[HPW][KC];
 #pragma unroll
-  for (int c = 0; c < KC; ++c)
-    qb[c] = *reinterpret_cast<const f16x8*>(qrow + 32 * c + 8 * lgrp);
+  for (int hh = 0; hh < HPW; ++hh) {
+    const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + h0 + hh) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qb[hh][c] = *reinterpret_cast<const f16x8*>(qrow + 32 * c + 8 * lgrp);
+  }
 
-  f32x4 o[DT];
+  f32x4 o[HPW][DT];
+  float m_row[HPW], l_row[HPW];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_row = -__builtin_huge_valf();
-  float l_row = 0.f;
+  for (int hh = 0; hh < HPW; ++hh) {
+#pragma unroll
+    for (int t = 0; t < DT; ++t) o[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_row[hh] = -__builtin_huge_valf();
+    l_row[hh] = 0.f;
+  }
 
   const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
   const int64_t tile_elems = (int64_t)16 * D;
   const int64_t head_off = (int64_t)g * tile_elems;
   const int64_t block_stride = (int64_t)num_kv_heads * tile_elems;
   const int used_blocks = (pos_hi >> 4) + 1;  // table entries this tile range may read
-  // Global -> registers for tile kt; tokens past pos_hi are zeros.  The tile's
-  // KT/16 block ids are work-group uniform (scalar loads), clamped into the pool.
+  // Pool offsets of the blocks of this work-group's first kIdTiles tiles,
+  // staged once (block ids clamped into the pool); later tiles read the
+  // table directly.
+  auto block_base = [&](int j) -> int64_t {
+    const uint32_t id = j < used_blocks ? (uint32_t)bt_row[j] : 0u;
+    return (int64_t)(id < (uint64_t)num_blocks ? id : num_blocks - 1) * block_stride + head_off;
+  };
+  for (int e = tid; e < S::kIdTiles * (KT / 16); e += 256) {
+    const int j = kt_begin * (KT / 16) + e;
+    if (j < kt_end * (KT / 16)) s_tile_base[e] = block_base(j);
+  }
+  __syncthreads();
+  // Global -> registers for tile kt; tokens past pos_hi are zeros.
   auto load_tile = [&](TileRegs& r, int kt) {
     const int tok0 = kt * KT;
     int64_t tile_base[KT / 16];
 #pragma unroll
     for (int b = 0; b < KT / 16; ++b) {
-      const int j = kt * (KT / 16) + b;
-      const uint32_t id = j < used_blocks ? (uint32_t)bt_row[j] : 0u;
-      tile_base[b] = (int64_t)(id < (uint64_t)num_blocks ? id : num_blocks - 1) * block_stride +
-                     head_off;
+      const int e = (kt - kt_begin) * (KT / 16) + b;
+      tile_base[b] = e < S::kIdTiles * (KT / 16) ? s_tile_base[e] : block_base(kt * (KT / 16) + b);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -193,51 +222,89 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     if (kt + 1 < kt_end) load_tile(next, kt + 1);  // in flight during this tile's math
     __syncthreads();
 
-    // S^T = K Q^T: s[t][e] = score of query row lrow with token tok0 + 16t + 4*lgrp + e.
-    f32x4 s[NT];
+    // S^T = K Q^T: s[hh][t][e] = score of head h0+hh, query row lrow, with
+    // token tok0 + 16t + 4*lgrp + e.  Each K fragment feeds HPW MFMAs.
+    f32x4 s[HPW][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) s[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
         const f16x8 a = *reinterpret_cast<const f16x8*>(k_lds + (16 * t + lrow) * S::KSTRIDE +
                                                          32 * c + 8 * lgrp);
-        s[t] = mfma16(a, qb[c], s[t]);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) s[hh][t] = mfma16(a, qb[hh][c], s[hh][t]);
       }
     }
-    float tile_max = -__builtin_huge_valf();
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = tok0 + 16 * t + 4 * lgrp + e;
-        const float x = tok <= my_pos ? s[t][e] * scale_log2 : -__builtin_huge_valf();
-        s[t][e] = x;
-        tile_max = fmaxf(tile_max, x);
-      }
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 16));
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
-    const float m_new = fmaxf(m_row, tile_max);
-    // A row that has seen no visible token yet keeps weight 0 (no -inf - -inf).
-    const float m_ref = m_new == -__builtin_huge_valf() ? 0.f : m_new;
-    const float alpha = fast_exp2(m_row - m_ref);
-    m_row = m_new;
-    l_row *= alpha;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) o[t] *= alpha;
 
-    // P^T as B operands: chunk c2 covers sub-tiles 2*c2 (elements 0..3) and 2*c2+1 (4..7).
-    f16x8 pb[NT / 2];
+    // Online softmax per (head, row), base 2.  Off the diagonal every token
+    // is visible and the scale goes into the exp's argument (one FMA per
+    // score, extreme taken on raw scores); on tiles that cross the diagonal
+    // of this work-group's rows the scores are scaled first and masked to
+    // -inf.  P^T as B operands: chunk c2 covers sub-tiles 2*c2 (elements
+    // 0..3) and 2*c2+1 (4..7), converted in pairs; l sums exactly the
+    // rounded weights.
+    const bool diagonal = tok0 + KT - 1 > p0 + tile_row0;
+    f16x8 pb[HPW][NT / 2];
 #pragma unroll
-    for (int c2 = 0; c2 < NT / 2; ++c2)
+    for (int hh = 0; hh < HPW; ++hh) {
+      float sc = scale_log2;
+      if (diagonal) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = fast_exp2(s[2 * c2 + e / 4][e % 4] - m_ref);
-        pb[c2][e] = (f16)p;
-        l_row += (float)pb[c2][e];
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = s[hh][t][e] * scale_log2;
+            s[hh][t][e] = tok0 + 16 * t + 4 * lgrp + e > my_pos ? -__builtin_huge_valf() : x;
+          }
+        sc = 1.f;
       }
+      float ext = s[hh][0][0];
+      if (sc >= 0.f) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ext = fmaxf(ext, s[hh][t][e]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ext = fminf(ext, s[hh][t][e]);
+      }
+      float tile_max = ext * sc;
+      tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 16));
+      tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+      // Lazy max: the reference only moves when a score passes it by more
+      // than kRescaleSlack (weights stay <= 2^8, exact in fp16 range), so
+      // after the first tiles the O rescale is skipped by the whole wave.
+      if (__any(tile_max > m_row[hh] + kRescaleSlack)) {
+        const float m_new = tile_max > m_row[hh] + kRescaleSlack ? tile_max : m_row[hh];
+        // A row that has seen no visible token keeps weight 0 (no -inf - -inf).
+        const float alpha = m_new == -__builtin_huge_valf() ? 1.f : fast_exp2(m_row[hh] - m_new);
+        m_row[hh] = m_new;
+        l_row[hh] *= alpha;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[hh][t] *= alpha;
+      }
+      const float neg_ref = m_row[hh] == -__builtin_huge_valf() ? 0.f : -m_row[hh];
+#pragma unroll
+      for (int c2 = 0; c2 < NT / 2; ++c2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4& sv = s[hh][2 * c2 + j / 2];
+          const float p0 = fast_exp2(__builtin_fmaf(sv[2 * (j % 2)], sc, neg_ref));
+          const float p1 = fast_exp2(__builtin_fmaf(sv[2 * (j % 2) + 1], sc, neg_ref));
+          w[j] = pack_h2_rtz(p0, p1);
+          l_row[hh] = dot2(w[j], kOnesH2, l_row[hh]);
+        }
+        pb[hh][c2] = __builtin_bit_cast(f16x8, uint4{w[0], w[1], w[2], w[3]});
+      }
+    }
 
-    // O^T += V^T P^T; A lane = d row 16*dt + lrow, tokens matching pb's order.
+    // O^T += V^T P^T; A lane = d row 16*dt + lrow, tokens matching pb's order;
+    // each V^T fragment feeds HPW MFMAs.
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -246,36 +313,45 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
         const uint4 packed = {lo.x, lo.y, hi.x, hi.y};
-        o[dt] = mfma16(__builtin_bit_cast(f16x8, packed), pb[c2], o[dt]);
+        const f16x8 a = __builtin_bit_cast(f16x8, packed);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) o[hh][dt] = mfma16(a, pb[hh][c2], o[hh][dt]);
       }
   }
 
-  l_row += __shfl_xor(l_row, 16);
-  l_row += __shfl_xor(l_row, 32);
-  if (!row_valid) return;
-  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-  const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + h;
-  if (num_splits == 1) {
-    uint16_t* dst = out + row_head * D + 4 * lgrp;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint2 w;
-      w.x = pack_h2_rne(o[dt][0] * inv, o[dt][1] * inv);
-      w.y = pack_h2_rne(o[dt][2] * inv, o[dt][3] * inv);
-      *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
-    }
-    return;
+  for (int hh = 0; hh < HPW; ++hh) {
+    l_row[hh] += __shfl_xor(l_row[hh], 16);
+    l_row[hh] += __shfl_xor(l_row[hh], 32);
   }
-  // Partial of this split: (o / l, m, l); l = 0 when no position was visible.
+  if (!row_valid) return;
   const int64_t first_row = query_start_loc[first_seq];
-  const int64_t pidx = ((row_base + my_row - first_row) * num_q_heads + h) * num_splits + split;
-  float* dst = part_o + pidx * D + 4 * lgrp;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[dt] * inv;
-  if (lane < 16) {
-    part_ml[pidx * 2] = m_row;
-    part_ml[pidx * 2 + 1] = l_row;
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float inv = l_row[hh] > 0.f ? 1.f / l_row[hh] : 0.f;
+    const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + h0 + hh;
+    if (num_splits == 1) {
+      uint16_t* dst = out + row_head * D + 4 * lgrp;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        uint2 w;
+        w.x = pack_h2_rne(o[hh][dt][0] * inv, o[hh][dt][1] * inv);
+        w.y = pack_h2_rne(o[hh][dt][2] * inv, o[hh][dt][3] * inv);
+        *reinterpret_cast<uint2*>(dst + 16 * dt) = w;
+      }
+      continue;
+    }
+    // Partial of this split: (o / l, m, l); l = 0 when no position was visible.
+    const int64_t pidx =
+        ((row_base + my_row - first_row) * num_q_heads + h0 + hh) * num_splits + split;
+    float* dst = part_o + pidx * D + 4 * lgrp;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(dst + 16 * dt) = o[hh][dt] * inv;
+    if (lane < 16) {
+      part_ml[pidx * 2] = m_row[hh];
+      part_ml[pidx * 2 + 1] = l_row[hh];
+    }
   }
 }
 
@@ -327,7 +403,8 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
       (int64_t)num_prefill_seqs * ((max_query_len + kRows - 1) / kRows) * num_q_heads;
   const int64_t kv_tiles = (max_context_len + kt - 1) / kt;
   // as many splits as fit in one round of resident work-groups (no tail round)
-  int64_t splits = kResidentGroups / groups;
+  const int64_t resident = kCUs * (head_dim == 128 ? kGroupsPerCU128 : kGroupsPerCU256);
+  int64_t splits = resident / groups;
   splits = std::min<int64_t>(std::min<int64_t>(splits, kMaxPrefillSplits), kv_tiles);
   plan.splits = (int32_t)std::max<int64_t>(splits, 1);
   plan.max_row_heads = (int64_t)num_prefill_seqs * max_query_len * num_q_heads;
@@ -356,12 +433,12 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
   const uint32_t x = ((max_query_len + kRows - 1) / kRows) * plan.splits;
   const dim3 grid((x + kXcds - 1) / kXcds * kXcds, num_q_heads, num_prefill_seqs);
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL(prefill_chunk_kernel<D>, grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, 1>), grid, dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                     static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads, num_q_heads,
-                     block_tables, max_blocks_per_seq, context_lens, query_start_loc, first_seq,
-                     ctx_clamp, plan.splits, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
-                     part_ml);
+                     static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+                     num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                     query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
+                     static_cast<uint16_t*>(out), part_o, part_ml);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return err;
   const int64_t waves = plan.max_row_heads;
