@@ -53,6 +53,10 @@ def parse():
                     help="force split-KV partition tokens (multiple of 64; 0 = automatic)")
     ap.add_argument("--separate", action="store_true",
                     help="append and attention as two calls per layer (default: one fused call)")
+    ap.add_argument("--schedule", choices=["auto", "on", "off"], default="auto",
+                    help="decode on the balanced schedule (on), on the fixed partition grid "
+                         "(off), or as the step chooses: the schedule only with prefill "
+                         "chunks (auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (5 times), the "
@@ -84,7 +88,8 @@ def measured_traffic(wl):
         return None
     fields = dict(line.split(": ", 1) for line in open(path) if ": " in line and not line.startswith(" "))
     h = hashlib.sha256()
-    for f in ("paged_kv_decode_append_amd/csrc/decode.hip", "paged_kv_decode_append_amd/csrc/device_util.h"):
+    for f in ("paged_kv_decode_append_amd/csrc/decode.hip", "paged_kv_decode_append_amd/csrc/decode_block.h",
+              "paged_kv_decode_append_amd/csrc/device_util.h"):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
         return None
@@ -153,7 +158,8 @@ def main():
     layers = [workloads.layer_tensors(wl, l, device="cuda") for l in range(wl.num_layers)]
     caches = [pkv.KVCache(t["k_pool"], t["v_pool"]) for t in layers]
     outs = [torch.empty_like(t["q"]) for t in layers]
-    step = Step.from_workload(wl, kv_partition_tokens=args.partition)
+    step = Step.from_workload(wl, kv_partition_tokens=args.partition,
+                              use_schedule={"auto": None, "on": True, "off": False}[args.schedule])
     torch.cuda.synchronize()
 
     fused = not args.separate
@@ -198,7 +204,8 @@ def main():
                                          step.query_start_loc, step.num_decode_seqs, step.scale,
                                          step.max_context_len, step.max_query_len,
                                          workspace=step.workspace,
-                                         kv_partition_tokens=step.kv_partition_tokens)
+                                         kv_partition_tokens=step.kv_partition_tokens,
+                                         schedule=step.schedule)
         ev[r][1].record(stream)
     torch.cuda.synchronize()
     attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3 / wl.num_layers

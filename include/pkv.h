@@ -18,6 +18,8 @@
  * attention, section "Where the batch size actually comes from").
  *
  * One step of one layer is:
+ *   0. pkv_decode_schedule -- balanced split of the decode work over the
+ *      GPU (optional; shared by all layers of the step);
  *   1. pkv_slot_mapping  -- pool slot of every new token (shared by all layers);
  *   2. pkv_kv_append     -- write each new token's K/V rows into its slot;
  *   3. pkv_paged_attention_step -- every new query token attends its own
@@ -158,6 +160,40 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
                                  size_t* bytes);
 
 /*
+ * Bytes of the per-step decode schedule buffer for these host hints (0 when
+ * the step is not schedulable: head_dim 256 (which keeps the partition
+ * grid), more than 16,384 (sequence, KV head) units, or no decode
+ * sequence).  Pure host function.
+ */
+int pkv_decode_schedule_size(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_context_len, size_t* bytes);
+
+/*
+ * Balanced schedule of the decode work of one step (danielfleming.xyz,
+ * "Static batching", section "Ragged batches": a ragged mix should cost only
+ * its real tokens).  Every (decode sequence, KV head) pair is a unit of
+ * ceil(ctx_i / 16) blocks; the units are laid end to end and cut into equal
+ * shares, one per decode work-group, so that short contexts are packed
+ * together and only long ones are split (and merged by log-sum-exp).  It
+ * depends only on the context lengths, so one schedule serves every layer
+ * of the step: build it once per step (after the context lengths are final,
+ * on the same stream), pass it to pkv_paged_attention_step /
+ * pkv_append_attention_step with the same num_decode_seqs, num_kv_heads,
+ * head_dim and max_context_len.
+ *
+ *   context_lens   device int32 [num_decode_seqs] (the step's, including the
+ *                  new token); read on the device only
+ *   schedule       device buffer of pkv_decode_schedule_size bytes (written)
+ * One launch of one work-group.  Does nothing when the size is 0.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_WORKSPACE (buffer too small),
+ * PKV_ERR_HIP.
+ */
+int pkv_decode_schedule(const int32_t* context_lens, int32_t num_decode_seqs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, void* schedule, size_t schedule_bytes,
+                        void* stream);
+
+/*
  * Paged attention over one layer for every new token of the step.
  *
  * Query row r of sequence i (row r = qsl[i] + k, k < n_i) sits at position
@@ -183,13 +219,21 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
  *   max_context_len, max_query_len, kv_partition_tokens
  *                    host hints, as for pkv_attention_workspace_size; the
  *                    split-KV plan is made from these alone (no device read)
+ *   schedule, schedule_bytes
+ *                    the step's pkv_decode_schedule buffer, or NULL / 0.  With
+ *                    a schedule, decode contexts that would be cut into
+ *                    partitions run on the balanced schedule instead; when
+ *                    every (sequence, KV head) fits one work-group the plain
+ *                    grid is used either way.  Ignored when
+ *                    kv_partition_tokens forces a partition size.
  *   workspace        device buffer of at least the size that
  *                    pkv_attention_workspace_size reports (may be NULL when
  *                    that size is 0); contents need not be initialised and
  *                    are undefined afterwards
- * Launches: the decode kernel (grid over sequence x KV head x partition),
- * the log-sum-exp merge of partitions when any sequence is split, and the
- * MFMA prefill kernel when prefill chunks are present; all on `stream`.
+ * Launches: the decode kernel (grid over sequence x KV head x partition, or
+ * one work-group per schedule share), the log-sum-exp merge of partitions or
+ * pieces when any context is split, and the MFMA prefill kernel (+ its merge)
+ * when prefill chunks are present; all on `stream`.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
  * PKV_ERR_HIP.
  */
@@ -199,8 +243,9 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
                              int32_t num_seqs, int32_t num_decode_seqs,
                              int32_t num_q_heads, float scale,
                              int32_t max_context_len, int32_t max_query_len,
-                             int32_t kv_partition_tokens,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             int32_t kv_partition_tokens, const void* schedule,
+                             size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /*
  * pkv_kv_append(cache, k_new, v_new, slot_mapping, num_tokens) followed by
@@ -228,8 +273,9 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
  *                  but the attention does not see it.
  *   num_tokens     rows of k_new / v_new / q (= qsl[num_seqs], or num_seqs
  *                  when query_start_loc is NULL); >= num_decode_seqs
- *   other arguments exactly as for pkv_paged_attention_step, with the same
- *                  workspace size (pkv_attention_workspace_size).
+ *   other arguments exactly as for pkv_paged_attention_step (schedule
+ *                  included), with the same workspace size
+ *                  (pkv_attention_workspace_size).
  * The rows of a sequence whose ctx_i < 1 are not written.
  * Errors: PKV_ERR_INVALID_ARG (also: k_new, v_new or slot_mapping NULL,
  * num_tokens inconsistent), PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
@@ -242,8 +288,9 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
                               const int32_t* query_start_loc, int32_t num_seqs,
                               int32_t num_decode_seqs, int32_t num_q_heads, float scale,
                               int32_t max_context_len, int32_t max_query_len,
-                              int32_t kv_partition_tokens, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              int32_t kv_partition_tokens, const void* schedule,
+                              size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Debug validator (host, synchronous, no GPU): checks on host copies of

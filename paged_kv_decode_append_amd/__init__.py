@@ -4,8 +4,9 @@ Argument marshalling only: every step of the path runs in the HIP kernels of
 libpkv.so; torch supplies device memory and the stream.  The names follow
 the C ABI in include/pkv.h without the ``pkv_`` prefix:
 
-    slot_mapping, kv_append, attention_workspace_size, paged_attention_step,
-    append_attention_step, validate_step, status_string, last_hip_error, version
+    slot_mapping, kv_append, attention_workspace_size, decode_schedule_size,
+    decode_schedule, paged_attention_step, append_attention_step, validate_step,
+    status_string, last_hip_error, version
 
 There is no fallback: importing this package without a built libpkv.so
 raises, and every call raises PkvError on a non-OK status.
@@ -30,8 +31,8 @@ PKV_ERR_CONTRACT = -5
 # every symbol include/pkv.h declares
 EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_hip_error", "pkv_slot_mapping", "pkv_kv_append",
-    "pkv_attention_workspace_size", "pkv_paged_attention_step", "pkv_append_attention_step",
-    "pkv_validate_step",
+    "pkv_attention_workspace_size", "pkv_decode_schedule_size", "pkv_decode_schedule",
+    "pkv_paged_attention_step", "pkv_append_attention_step", "pkv_validate_step",
 )
 
 
@@ -71,12 +72,14 @@ def _load():
     lib.pkv_kv_append.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P]
     lib.pkv_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                                  ctypes.POINTER(ctypes.c_size_t)]
+    sz = ctypes.c_size_t
+    lib.pkv_decode_schedule_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.pkv_decode_schedule.argtypes = [P, i32, i32, i32, i32, i32, P, sz, P]
     lib.pkv_paged_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, i32, i32,
-                                             i32, ctypes.c_float, i32, i32, i32, P,
-                                             ctypes.c_size_t, P]
+                                             i32, ctypes.c_float, i32, i32, i32, P, sz, P, sz, P]
     lib.pkv_append_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, P, i32,
                                               P, P, i32, i32, i32, ctypes.c_float, i32, i32, i32,
-                                              P, ctypes.c_size_t, P]
+                                              P, sz, P, sz, P]
     lib.pkv_validate_step.argtypes = [P, i32, P, P, i32, i32, i64, i32, P, i32, i32, i32,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     for name in EXPORTED:
@@ -207,10 +210,44 @@ def attention_workspace_size(num_seqs, num_decode_seqs, num_q_heads, num_kv_head
     return int(out.value)
 
 
+def decode_schedule_size(num_decode_seqs, num_kv_heads, head_dim, max_context_len) -> int:
+    """pkv_decode_schedule_size: bytes of the per-step decode schedule (0: not used)."""
+    out = ctypes.c_size_t(0)
+    rc = lib.pkv_decode_schedule_size(num_decode_seqs, num_kv_heads, head_dim, max_context_len,
+                                      ctypes.byref(out))
+    _check(rc, "pkv_decode_schedule_size")
+    return int(out.value)
+
+
+def decode_schedule(context_lens, num_decode_seqs: int, num_kv_heads: int, head_dim: int,
+                    max_blocks_per_seq: int, max_context_len: int, schedule, stream=None):
+    """pkv_decode_schedule: balanced split of the step's decode work into `schedule`
+    (uint8 device tensor of decode_schedule_size bytes)."""
+    import torch
+    _need(context_lens, torch.int32, "context_lens")
+    nbytes = 0
+    if schedule is not None:
+        _need(schedule, torch.uint8, "schedule")
+        nbytes = schedule.numel()
+    rc = lib.pkv_decode_schedule(_ptr(context_lens), num_decode_seqs, num_kv_heads, head_dim,
+                                 max_blocks_per_seq, max_context_len, _ptr(schedule), nbytes,
+                                 _stream(stream))
+    _check(rc, "pkv_decode_schedule")
+    return schedule
+
+
+def _schedule_args(schedule):
+    import torch
+    if schedule is None:
+        return None, 0
+    _need(schedule, torch.uint8, "schedule")
+    return _ptr(schedule), schedule.numel()
+
+
 def paged_attention_step(cache: KVCache, q, out, block_tables, context_lens, query_start_loc,
                          num_decode_seqs: int, scale: float, max_context_len: int,
                          max_query_len: int, workspace=None, kv_partition_tokens: int = 0,
-                         stream=None):
+                         stream=None, schedule=None):
     """pkv_paged_attention_step over one layer; q/out fp16 [T, Hq, d]."""
     import torch
     _need(q, torch.float16, "q")
@@ -225,11 +262,13 @@ def paged_attention_step(cache: KVCache, q, out, block_tables, context_lens, que
     if workspace is not None:
         _need(workspace, torch.uint8, "workspace")
         ws_bytes = workspace.numel()
+    sched_ptr, sched_bytes = _schedule_args(schedule)
     rc = lib.pkv_paged_attention_step(
         ctypes.byref(cache._c), _ptr(q), _ptr(out), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), _ptr(query_start_loc), context_lens.shape[0], num_decode_seqs,
         q.shape[1], float(scale), int(max_context_len), int(max_query_len),
-        int(kv_partition_tokens), _ptr(workspace), ws_bytes, _stream(stream))
+        int(kv_partition_tokens), sched_ptr, sched_bytes, _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check(rc, "pkv_paged_attention_step")
     return out
 
@@ -237,7 +276,7 @@ def paged_attention_step(cache: KVCache, q, out, block_tables, context_lens, que
 def append_attention_step(cache: KVCache, k_new, v_new, slot_mapping_t, q, out, block_tables,
                           context_lens, query_start_loc, num_decode_seqs: int, scale: float,
                           max_context_len: int, max_query_len: int, workspace=None,
-                          kv_partition_tokens: int = 0, stream=None):
+                          kv_partition_tokens: int = 0, stream=None, schedule=None):
     """pkv_append_attention_step: kv_append then paged_attention_step in one
     call, the decode tokens appended inside the decode kernel."""
     import torch
@@ -263,8 +302,8 @@ def append_attention_step(cache: KVCache, k_new, v_new, slot_mapping_t, q, out, 
         ctypes.byref(cache._c), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping_t), T, _ptr(q),
         _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         _ptr(query_start_loc), context_lens.shape[0], num_decode_seqs, q.shape[1], float(scale),
-        int(max_context_len), int(max_query_len), int(kv_partition_tokens), _ptr(workspace),
-        ws_bytes, _stream(stream))
+        int(max_context_len), int(max_query_len), int(kv_partition_tokens),
+        *_schedule_args(schedule), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_append_attention_step")
     return out
 

@@ -5,6 +5,8 @@
 // machine without one.  Device arrays are never read from the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <unordered_set>
 #include <vector>
@@ -123,10 +125,46 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, num_kv_heads, num_q_heads, head_dim,
                                           max_context_len, kv_partition_tokens);
   if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  const pkv::DecodeSchedulePlan splan = pkv::plan_decode_schedule(
+      num_decode_seqs, num_kv_heads, num_q_heads, head_dim, max_context_len);
+  if (kv_partition_tokens == 0)  // either decode path may run
+    plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
   const pkv::PrefillPlan pplan = pkv::plan_prefill(num_seqs - num_decode_seqs, num_q_heads,
                                                    head_dim, max_context_len, max_query_len);
   *bytes = workspace_layout(plan, pplan);
   return PKV_OK;
+}
+
+int pkv_decode_schedule_size(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_context_len, size_t* bytes) {
+  if (!bytes || num_decode_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  *bytes = pkv::plan_decode_schedule(num_decode_seqs, num_kv_heads, num_kv_heads, head_dim,
+                                     max_context_len).schedule_bytes;
+  return PKV_OK;
+}
+
+int pkv_decode_schedule(const int32_t* context_lens, int32_t num_decode_seqs,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, void* schedule, size_t schedule_bytes,
+                        void* stream) {
+  if (num_decode_seqs < 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * kBlockSize)
+    return PKV_ERR_INVALID_ARG;
+  const pkv::DecodeSchedulePlan splan = pkv::plan_decode_schedule(
+      num_decode_seqs, num_kv_heads, num_kv_heads, head_dim, max_context_len);
+  if (splan.num_groups == 0) return PKV_OK;  // nothing to schedule (partition path)
+  if (!context_lens || !schedule) return PKV_ERR_INVALID_ARG;
+  if (schedule_bytes < splan.schedule_bytes) return PKV_ERR_WORKSPACE;
+  const int32_t ctx_clamp =
+      (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * kBlockSize, INT32_MAX);
+  return from_hip(pkv::launch_decode_schedule(context_lens, num_decode_seqs, num_kv_heads,
+                                              ctx_clamp, splan, schedule,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
@@ -142,7 +180,8 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
                    const int32_t* context_lens, const int32_t* query_start_loc,
                    int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_heads, float scale,
                    int32_t max_context_len, int32_t max_query_len, int32_t kv_partition_tokens,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   const void* schedule, size_t schedule_bytes, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   int rc = check_cache(cache);
   if (rc != PKV_OK) return rc;
   rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, cache->num_kv_heads,
@@ -165,6 +204,16 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, cache->num_kv_heads, num_q_heads,
                                           cache->head_dim, max_context_len, kv_partition_tokens);
   if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  const pkv::DecodeSchedulePlan splan = pkv::plan_decode_schedule(
+      num_decode_seqs, cache->num_kv_heads, num_q_heads, cache->head_dim, max_context_len);
+  // The balanced schedule replaces the partition grid whenever the latter
+  // would cut contexts (and was not forced by kv_partition_tokens); when
+  // every (sequence, KV head) fits one work-group of a single round, the
+  // partition grid needs no merge and is kept.
+  const bool scheduled = schedule != nullptr && splan.num_groups > 0 &&
+                         kv_partition_tokens == 0 && plan.max_parts > 1;
+  if (scheduled && schedule_bytes < splan.schedule_bytes) return PKV_ERR_WORKSPACE;
+  if (kv_partition_tokens == 0) plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
   const pkv::PrefillPlan pplan = pkv::plan_prefill(num_prefill, num_q_heads, cache->head_dim,
                                                    max_context_len, max_query_len);
   const size_t need = workspace_layout(plan, pplan);
@@ -182,10 +231,16 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
     if (rc != PKV_OK) return rc;
   }
   const pkv::DecodeAppend app{k_new, v_new, fused ? slot_mapping : nullptr};
-  rc = from_hip(pkv::launch_paged_decode(
-      q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
-      cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
-      plan, app, out, workspace, s));
+  if (scheduled)
+    rc = from_hip(pkv::launch_paged_decode_scheduled(
+        q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
+        cache->head_dim, block_tables, max_blocks_per_seq, num_decode_seqs, scale, splan,
+        schedule, app, out, workspace, s));
+  else
+    rc = from_hip(pkv::launch_paged_decode(
+        q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
+        cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
+        plan, app, out, workspace, s));
   if (rc != PKV_OK) return rc;
   return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, cache->num_blocks,
                                       cache->num_kv_heads, num_q_heads, cache->head_dim,
@@ -204,12 +259,14 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
                              int32_t num_seqs, int32_t num_decode_seqs,
                              int32_t num_q_heads, float scale,
                              int32_t max_context_len, int32_t max_query_len,
-                             int32_t kv_partition_tokens,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t kv_partition_tokens, const void* schedule,
+                             size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   return attention_step(cache, nullptr, nullptr, nullptr, 0, q, out, block_tables,
                         max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
                         num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
-                        kv_partition_tokens, workspace, workspace_bytes, stream);
+                        kv_partition_tokens, schedule, schedule_bytes, workspace,
+                        workspace_bytes, stream);
 }
 
 int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
@@ -219,13 +276,15 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
                               const int32_t* query_start_loc, int32_t num_seqs,
                               int32_t num_decode_seqs, int32_t num_q_heads, float scale,
                               int32_t max_context_len, int32_t max_query_len,
-                              int32_t kv_partition_tokens, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              int32_t kv_partition_tokens, const void* schedule,
+                              size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (!k_new) return PKV_ERR_INVALID_ARG;
   return attention_step(cache, k_new, v_new, slot_mapping, num_tokens, q, out, block_tables,
                         max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
                         num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
-                        kv_partition_tokens, workspace, workspace_bytes, stream);
+                        kv_partition_tokens, schedule, schedule_bytes, workspace,
+                        workspace_bytes, stream);
 }
 
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -45,6 +45,32 @@ hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_
                                const DecodePlan& plan, const DecodeAppend& app, void* out,
                                void* workspace, hipStream_t stream);
 
+// Balanced decode schedule (decode_sched.hip): made once per step on the
+// device from the context lengths, read by every layer's decode launch.
+struct DecodeSchedulePlan {
+  int32_t num_groups;     // decode work-groups (0: not schedulable, use the partition path)
+  size_t schedule_bytes;  // size of the schedule buffer
+  size_t partial_bytes;   // workspace for the pieces of split units
+};
+
+DecodeSchedulePlan plan_decode_schedule(int32_t num_decode_seqs, int32_t num_kv_heads,
+                                        int32_t num_q_heads, int32_t head_dim,
+                                        int32_t max_context_len);
+
+hipError_t launch_decode_schedule(const int32_t* context_lens, int32_t num_decode_seqs,
+                                  int32_t num_kv_heads, int32_t ctx_clamp,
+                                  const DecodeSchedulePlan& plan, void* schedule,
+                                  hipStream_t stream);
+
+hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_pool,
+                                         int64_t num_blocks, int32_t num_kv_heads,
+                                         int32_t num_q_heads, int32_t head_dim,
+                                         const int32_t* block_tables,
+                                         int32_t max_blocks_per_seq, int32_t num_decode_seqs,
+                                         float scale, const DecodeSchedulePlan& plan,
+                                         const void* schedule, const DecodeAppend& app,
+                                         void* out, void* workspace, hipStream_t stream);
+
 // Split-KV plan of the prefill chunks: each 64-row query tile is cut into
 // `splits` ranges of context tiles, merged by log-sum-exp when splits > 1.
 struct PrefillPlan {

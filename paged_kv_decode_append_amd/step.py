@@ -5,6 +5,8 @@ Batching Is Not a Bigger Batch", section "What the scheduler does on one
 step"), so block tables, context lengths and query offsets are step-level
 metadata shared by every layer, while the pools are per layer.  Per step:
 
+    pkv_decode_schedule                   (once, when the step uses the balanced
+                                           split of the decode work)
     pkv_slot_mapping                      (once)
     for every layer:
         pkv_append_attention_step         (this layer's new K/V into its pool,
@@ -13,19 +15,27 @@ metadata shared by every layer, while the pools are per layer.  Per step:
         pkv_kv_append ; pkv_paged_attention_step
 
 all enqueued on one stream; append precedes attention within a layer.
+
+The balanced schedule is used by default only in steps that carry prefill
+chunks.  There the one context-length hint of the attention call covers the
+chunk's context, so the fixed partition grid would be cut for a context longer
+than any decode has and would leave much of the GPU idle; the schedule is cut
+from the actual context lengths on the device.  In pure decode steps the grid
+is cut from the true longest context, and on the measured workloads it is the
+faster of the two.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import (KVCache, append_attention_step, attention_workspace_size, kv_append,
-               paged_attention_step, slot_mapping)
+from . import (KVCache, append_attention_step, attention_workspace_size, decode_schedule,
+               decode_schedule_size, kv_append, paged_attention_step, slot_mapping)
 
 
 class Step:
     def __init__(self, block_tables, context_lens, new_tokens, num_decode_seqs: int,
                  num_q_heads: int, num_kv_heads: int, head_dim: int, scale: float,
-                 kv_partition_tokens: int = 0, device="cuda"):
+                 kv_partition_tokens: int = 0, device="cuda", use_schedule: bool | None = None):
         import torch
 
         bt = np.ascontiguousarray(block_tables, dtype=np.int32)
@@ -50,15 +60,28 @@ class Step:
                                       self.max_query_len, self.kv_partition_tokens)
         self.workspace_bytes = ws
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.max_blocks_per_seq = int(bt.shape[1])
+        if use_schedule is None:
+            use_schedule = not pure_decode
+        sb = decode_schedule_size(self.num_decode_seqs, num_kv_heads, head_dim,
+                                  self.max_context_len) if use_schedule else 0
+        self.schedule = torch.empty(sb, dtype=torch.uint8, device=device) if sb else None
 
     @classmethod
-    def from_workload(cls, wl, kv_partition_tokens: int = 0, device="cuda"):
+    def from_workload(cls, wl, kv_partition_tokens: int = 0, device="cuda",
+                      use_schedule: bool | None = None):
         return cls(wl.block_tables, wl.context_lens, wl.new_tokens, wl.num_decode_seqs,
                    wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.scale,
-                   kv_partition_tokens=kv_partition_tokens, device=device)
+                   kv_partition_tokens=kv_partition_tokens, device=device,
+                   use_schedule=use_schedule)
 
     def plan(self, stream=None):
-        """Slot of every new token (once per step, shared by all layers)."""
+        """Per-step work shared by all layers: the balanced decode schedule
+        (when the step has one) and the slot of every new token."""
+        if self.schedule is not None:
+            decode_schedule(self.context_lens, self.num_decode_seqs, self.num_kv_heads,
+                            self.head_dim, self.max_blocks_per_seq, self.max_context_len,
+                            self.schedule, stream=stream)
         slot_mapping(self.block_tables, self.context_lens, self.query_start_loc, self.num_tokens,
                      self.slot_mapping, stream=stream)
 
@@ -69,11 +92,13 @@ class Step:
                 cache, k_new, v_new, self.slot_mapping, q, out, self.block_tables,
                 self.context_lens, self.query_start_loc, self.num_decode_seqs, self.scale,
                 self.max_context_len, self.max_query_len, workspace=self.workspace,
-                kv_partition_tokens=self.kv_partition_tokens, stream=stream)
+                kv_partition_tokens=self.kv_partition_tokens, stream=stream,
+                schedule=self.schedule)
         kv_append(cache, k_new, v_new, self.slot_mapping, stream=stream)
         paged_attention_step(cache, q, out, self.block_tables, self.context_lens,
                              self.query_start_loc, self.num_decode_seqs, self.scale,
                              self.max_context_len, self.max_query_len,
                              workspace=self.workspace,
-                             kv_partition_tokens=self.kv_partition_tokens, stream=stream)
+                             kv_partition_tokens=self.kv_partition_tokens, stream=stream,
+                             schedule=self.schedule)
         return out

@@ -72,7 +72,8 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison: bool = True,
-                        seq_subset=None, tensors=None, row_samples=None, fused: bool = True):
+                        seq_subset=None, tensors=None, row_samples=None, fused: bool = True,
+                        step=None, use_schedule=None):
     """One layer of one step on the GPU, checked against the oracle.
 
     fused: the layer runs as pkv_append_attention_step (the benchmark's
@@ -91,7 +92,9 @@ def run_layer_and_check(wl, layer: int = 0, kv_partition_tokens: int = 0, poison
     kp0, vp0 = host_bits(t["k_pool"]), host_bits(t["v_pool"])
     q, kn, vn = host_bits(t["q"]), host_bits(t["k_new"]), host_bits(t["v_new"])
 
-    step = Step.from_workload(wl, kv_partition_tokens=kv_partition_tokens)
+    if step is None:
+        step = Step.from_workload(wl, kv_partition_tokens=kv_partition_tokens,
+                                  use_schedule=use_schedule)
     step.plan()
     cache = pkv.KVCache(t["k_pool"], t["v_pool"])
     out = torch.full_like(t["q"], float("nan"))

@@ -65,7 +65,7 @@ def test_slot_mapping_argument_errors():
 def _step(cache, q=FAKE, out=FAKE, bt=FAKE, maxblk=64, ctx=FAKE, qsl=None, nseq=4, ndec=4, hq=12,
           scale=0.1, mcl=1024, mql=1, part=0, ws=None, wsb=0):
     return pkv.lib.pkv_paged_attention_step(ctypes.byref(cache), q, out, bt, maxblk, ctx, qsl, nseq,
-                                            ndec, hq, scale, mcl, mql, part, ws, wsb, None)
+                                            ndec, hq, scale, mcl, mql, part, None, 0, ws, wsb, None)
 
 
 def test_attention_step_argument_errors():
@@ -91,7 +91,7 @@ def _fused(cache, kn=FAKE, vn=FAKE, slots=FAKE, T=4, q=FAKE, out=FAKE, bt=FAKE, 
            wsb=0):
     return pkv.lib.pkv_append_attention_step(ctypes.byref(cache), kn, vn, slots, T, q, out, bt,
                                              maxblk, ctx, qsl, nseq, ndec, hq, scale, mcl, mql,
-                                             part, ws, wsb, None)
+                                             part, None, 0, ws, wsb, None)
 
 
 def test_fused_step_argument_errors():
@@ -105,6 +105,28 @@ def test_fused_step_argument_errors():
     assert _fused(c, hq=18) == -2
     assert _fused(c, mcl=4096, maxblk=256) == pkv.PKV_ERR_WORKSPACE
     assert _fused(c, nseq=0, ndec=0, T=0) == pkv.PKV_OK
+
+
+def test_decode_schedule_size_and_argument_errors():
+    # d = 128 steps get a schedule; d = 256 keeps the partition grid
+    assert pkv.decode_schedule_size(83, 2, 128, 4352) > 0
+    assert pkv.decode_schedule_size(4, 4, 256, 262144) == 0
+    assert pkv.decode_schedule_size(0, 2, 128, 1) == 0
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_schedule_size(4, 2, 64, 100)           # unsupported head_dim
+    lib = pkv.lib
+    need = pkv.decode_schedule_size(83, 2, 128, 4352)
+    assert lib.pkv_decode_schedule(None, 83, 2, 128, 272, 4352, FAKE, need, None) == -1
+    assert lib.pkv_decode_schedule(FAKE, 83, 2, 128, 272, 4352, None, need, None) == -1
+    assert lib.pkv_decode_schedule(FAKE, 83, 2, 128, 272, 4352, FAKE, need - 1, None) == \
+        pkv.PKV_ERR_WORKSPACE
+    assert lib.pkv_decode_schedule(FAKE, 83, 2, 128, 200, 4352, FAKE, need, None) == -1  # row too short
+    assert lib.pkv_decode_schedule(FAKE, 83, 2, 256, 272, 4352, FAKE, 0, None) == 0    # nothing to do
+    # a schedule smaller than the plan's is refused by the step
+    c = _cache()
+    assert pkv.lib.pkv_paged_attention_step(ctypes.byref(c), FAKE, FAKE, FAKE, 256, FAKE, None, 4,
+                                            4, 12, 0.1, 4096, 1, 0, FAKE, 16, FAKE, 1 << 30,
+                                            None) == pkv.PKV_ERR_WORKSPACE
 
 
 def test_workspace_size_is_host_only_and_monotone():

@@ -169,12 +169,14 @@ def test_fused_and_separate_append_give_identical_bits(d, hq, hkv, part):
 def _fused_call(wl, t, slots, part=0):
     from paged_kv_decode_append_amd.step import Step
     step = Step.from_workload(wl, kv_partition_tokens=part)
+    step.plan()  # the decode schedule (the slot mapping it also writes is not used)
     out = torch.empty_like(t["q"])
     pkv.append_attention_step(pkv.KVCache(t["k_pool"], t["v_pool"]), t["k_new"], t["v_new"],
                               torch.from_numpy(slots).cuda(), t["q"], out, step.block_tables,
                               step.context_lens, step.query_start_loc, wl.num_decode_seqs,
                               wl.scale, step.max_context_len, step.max_query_len,
-                              workspace=step.workspace, kv_partition_tokens=part)
+                              workspace=step.workspace, kv_partition_tokens=part,
+                              schedule=step.schedule)
     torch.cuda.synchronize()
     return out
 
