@@ -17,7 +17,14 @@ roofline   = the dominant kernel (paged decode + its merge): algorithmic
              bytes per launch (KV of every context, Q and O, block ids, and
              the appended rows when fused) over the launch's average
              duration from HIP events around back-to-back attention
-             launches, against the 8 TB/s HBM peak.
+             launches, against the 8 TB/s HBM peak; also against the rate of
+             a plain device copy moving the same number of bytes
+             (measured_copy_gbps, frac_of_measured_copy).
+ms_per_step_median / _min = per-step durations from events between the timed
+             steps.
+prefill    = (steps with prefill chunks) the chunks alone timed the same
+             way: flops per launch over launch time against the dense fp16
+             MFMA peak; query_tokens_per_s counts every new token of the step.
 cpu_baseline = the fp64 CPU oracle, timed on the host on a bounded sample of
              the same workload (a few layers of the step), scaled to a step.
 """
@@ -37,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged-attn step: KV-read HBM GB/s (% of peak) and decode tokens/s at 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak (no sparsity)
 DEFAULT_WORKLOAD = "qwen_uniform"
 
 
@@ -94,6 +102,65 @@ def measured_traffic(wl):
     if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def measured_copy_rate(nbytes: int) -> float:
+    """GB/s of a plain device-to-device copy moving `nbytes` in total (half
+    read, half written): the rate HBM gives a trivially streaming kernel of
+    the same size, with its own launch ramp and drain."""
+    import torch
+    half = max(nbytes // 2, 1 << 20)
+    src = torch.ones(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    times = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3)
+    return 2 * half / float(np.median(times)) / 1e9
+
+
+def prefill_roofline(wl, caches, layers, outs):
+    """The prefill chunks alone (split-KV prefill kernel + its merge), timed
+    with HIP events over L back-to-back launches: achieved TFLOP/s against
+    the dense fp16 MFMA peak."""
+    import torch
+    import paged_kv_decode_append_amd as pkv
+    from paged_kv_decode_append_amd.step import Step
+
+    B = wl.num_decode_seqs
+    pre = Step(wl.block_tables[B:], wl.context_lens[B:], wl.new_tokens[B:], 0, wl.num_q_heads,
+               wl.num_kv_heads, wl.head_dim, wl.scale)
+    pre.plan()
+    stream = torch.cuda.current_stream()
+
+    def launch_all():
+        for c, t, o in zip(caches, layers, outs):
+            pkv.paged_attention_step(c, t["q"][B:], o[B:], pre.block_tables, pre.context_lens,
+                                     pre.query_start_loc, 0, wl.scale, pre.max_context_len,
+                                     pre.max_query_len, workspace=pre.workspace)
+
+    launch_all()
+    times = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch_all()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e-3 / wl.num_layers)
+    t = float(np.mean(times))
+    flops = wl.prefill_flops_per_layer()
+    return {"bound": "mfma", "flop_per_launch": flops, "launch_us": round(t * 1e6, 2),
+            "achieved": round(flops / t / 1e12, 2), "peak": MFMA_FP16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / MFMA_FP16_PEAK_TFLOPS, 4),
+            "kernel": "chunked-prefill attention on MFMA (+ its split-KV merge)"}
 
 
 def cpu_baseline(wl, layer_tensors_dev, budget_s: float):
@@ -173,20 +240,25 @@ def main():
         run_step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K steps between synchronisations.
+    # Timed region: exactly K steps between synchronisations; an event between
+    # steps (no synchronisation) gives the per-step spread.
+    stream = torch.cuda.current_stream()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for k in range(args.steps):
         run_step()
+        marks[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
+    step_ms = [marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps)]
 
     # Per-launch duration of the attention (decode + merge [+ prefill]) with HIP
     # events on the launch stream, in a separate pass so that events do not
     # perturb the step timing above: the L layers' attention calls run back
     # to back between two events (fused: the whole step is those calls; when
     # separate, each pass appends every layer first).
-    stream = torch.cuda.current_stream()
     reps = min(args.steps, 20)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -212,6 +284,8 @@ def main():
 
     alg_bytes = algorithmic_bytes_per_attention_launch(wl, fused)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
+    copy_gbps = measured_copy_rate(alg_bytes)
+    prefill = prefill_roofline(wl, caches, layers, outs) if wl.num_decode_seqs < wl.num_seqs else None
     kv_bytes_step = wl.kv_read_bytes_per_layer(decode_only=True) * wl.num_layers
     result = {
         "metric": METRIC,
@@ -221,6 +295,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(np.min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -253,9 +329,14 @@ def main():
                       " (+ split-KV merge when split)",
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
+            "measured_copy_gbps": round(copy_gbps, 1),
+            "frac_of_measured_copy": round(achieved / copy_gbps, 4),
         },
         "kv_read_gbps_step": round(kv_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
     }
+    if prefill is not None:
+        result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
+        result["prefill"] = prefill
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -120,6 +120,15 @@ class Workload:
         t = self.num_decode_seqs if decode_only else self.num_tokens
         return 2 * t * self.num_q_heads * self.head_dim * FP16_BYTES
 
+    def prefill_flops_per_layer(self) -> int:
+        """4 x d x Hq flops per (query row, attended position) of the prefill
+        chunks (S = QK^T and O = PV, 2 flops per multiply-add), causal: row k
+        of a chunk of n rows ending at ctx attends ctx - n + k + 1 positions."""
+        ctx = self.context_lens[self.num_decode_seqs:].astype(np.int64)
+        n = self.new_tokens[self.num_decode_seqs:].astype(np.int64)
+        pairs = int((n * (ctx - n + 1) + n * (n - 1) // 2).sum())
+        return 4 * self.head_dim * self.num_q_heads * pairs
+
     def append_bytes_per_layer(self) -> int:
         return 2 * self.num_tokens * self.num_kv_heads * self.head_dim * FP16_BYTES
 
