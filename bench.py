@@ -65,6 +65,9 @@ def parse():
                     help="decode on the balanced schedule (on), on the fixed partition grid "
                          "(off), or as the step chooses: the schedule only with prefill "
                          "chunks (auto)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the whole step (all layers) once as a HIP graph and time "
+                         "its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (5 times), the "
@@ -236,6 +239,12 @@ def main():
         for c, t, o in zip(caches, layers, outs):
             step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=fused)
 
+    if args.graph:
+        run_step()
+        graph = step.capture([(c, t["q"], t["k_new"], t["v_new"], o)
+                              for c, t, o in zip(caches, layers, outs)], fused=fused)
+        run_step = graph.replay
+
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -316,6 +325,7 @@ def main():
             "pool_blocks_per_layer": wl.num_blocks,
             "parallelism": "single-gpu",
             "append": "fused into the decode kernel" if fused else "separate kernel",
+            "launch": "one HIP graph per step" if args.graph else "one library call per layer",
         },
         "roofline": {
             "bound": "hbm",

@@ -15,6 +15,13 @@ metadata shared by every layer, while the pools are per layer.  Per step:
         pkv_kv_append ; pkv_paged_attention_step
 
 all enqueued on one stream; append precedes attention within a layer.
+`Step.capture` records that whole sequence once as a HIP graph, so a step
+costs one graph launch on the host instead of 1 + L (or 2 + 2L) library
+calls ([SB] "What changed": per-pass launch overhead is what grows with the
+number of launches).  The library's calls only enqueue kernels (no
+allocation, no memset, no synchronisation), which is what makes them
+capturable; the graph keeps the buffers' addresses, so a replay reads and
+writes the same tensors, whose contents the caller refreshes between steps.
 
 The balanced schedule is used by default only in steps that carry prefill
 chunks.  There the one context-length hint of the attention call covers the
@@ -84,6 +91,23 @@ class Step:
                             self.schedule, stream=stream)
         slot_mapping(self.block_tables, self.context_lens, self.query_start_loc, self.num_tokens,
                      self.slot_mapping, stream=stream)
+
+    def capture(self, layers, fused: bool = True):
+        """One HIP graph of the whole step: plan() then every layer's call.
+
+        layers: per layer (cache, q, k_new, v_new, out).  Returns a
+        torch.cuda.CUDAGraph; graph.replay() enqueues the step on the current
+        stream.  Nothing is allocated during capture."""
+        import torch
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(graph, stream=side):
+            self.plan()
+            for cache, q, k_new, v_new, out in layers:
+                self.layer(cache, q, k_new, v_new, out, fused=fused)
+        torch.cuda.current_stream().wait_stream(side)
+        return graph
 
     def layer(self, cache: KVCache, q, k_new, v_new, out, stream=None, fused: bool = True):
         """Append this layer's new K/V, then attend (one call when fused)."""
