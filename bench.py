@@ -11,8 +11,9 @@ Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--separate]
 
-value      = decode tokens per second of the whole step (decode sequences x
-             steps / wall time), wall time between synchronisations.
+value      = decode tokens per second of the whole step (query tokens of the
+             decode and multi-token-decode sequences x steps / wall time),
+             wall time between synchronisations.
 roofline   = the dominant kernel (paged decode + its merge): algorithmic
              bytes per launch (KV of every context, Q and O, block ids, and
              the appended rows when fused) over the launch's average
@@ -77,16 +78,24 @@ def parse():
 
 
 def algorithmic_bytes_per_attention_launch(wl, fused: bool) -> int:
-    """KV of every decode context + Q and O rows + block ids, one layer; when
-    the decode tokens are appended in the same kernel, + their K/V rows read
-    and written and their slots."""
-    B = wl.num_decode_seqs
-    ctx = wl.context_lens[:B].astype(np.int64)
+    """For the sequences whose attention streams the cache (decodes, and
+    multi-token decodes whose G x n rows fit one tile): KV of every context +
+    Q and O rows + block ids, one layer; when the call also appends their new
+    tokens, + those K/V rows read and written and their slots."""
+    m = wl.short_chunk()
+    ctx = wl.context_lens[m].astype(np.int64)
+    T = int(wl.new_tokens[m].sum())
     kv = int(ctx.sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
-    qo = 2 * B * wl.num_q_heads * wl.head_dim * 2
+    qo = 2 * T * wl.num_q_heads * wl.head_dim * 2
     ids = int((-(-ctx // wl.block_size)).sum()) * 4
-    app = (2 * 2 * B * wl.num_kv_heads * wl.head_dim * 2 + 8 * B) if fused else 0
+    app = (2 * 2 * T * wl.num_kv_heads * wl.head_dim * 2 + 8 * T) if fused else 0
     return kv + qo + ids + app
+
+
+def streamed_tokens(wl) -> int:
+    """Query tokens of the sequences whose attention streams the cache: one
+    per decode sequence, n per multi-token decode."""
+    return int(wl.new_tokens[wl.short_chunk()].sum())
 
 
 def measured_traffic(wl):
@@ -186,7 +195,7 @@ def cpu_baseline(wl, layer_tensors_dev, budget_s: float):
             break
     per_step = spent / layers * wl.num_layers
     return {
-        "value": wl.num_decode_seqs / per_step,
+        "value": streamed_tokens(wl) / per_step,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
@@ -294,11 +303,19 @@ def main():
     alg_bytes = algorithmic_bytes_per_attention_launch(wl, fused)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
     copy_gbps = measured_copy_rate(alg_bytes)
-    prefill = prefill_roofline(wl, caches, layers, outs) if wl.num_decode_seqs < wl.num_seqs else None
-    kv_bytes_step = wl.kv_read_bytes_per_layer(decode_only=True) * wl.num_layers
+    long_chunks = not wl.short_chunk().all()
+    prefill = prefill_roofline(wl, caches, layers, outs) if long_chunks else None
+    kv_bytes_step = (int(wl.context_lens[wl.short_chunk()].astype(np.int64).sum()) *
+                     wl.num_kv_heads * wl.head_dim * 2 * 2 * wl.num_layers)
+    multi = wl.num_decode_seqs < int(wl.short_chunk().sum())
+    kernel = ("paged decode attention with the decode tokens' append fused in"
+              if fused else "paged decode attention") + " (+ split-KV merge when split)"
+    if multi:
+        kernel += ("; multi-token decodes on the packed-row MFMA kernel (+ its merge)" +
+                   (" after their append" if fused else ""))
     result = {
         "metric": METRIC,
-        "value": round(wl.num_decode_seqs / (ms_per_step * 1e-3), 1),
+        "value": round(streamed_tokens(wl) / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -316,6 +333,7 @@ def main():
             "layers": wl.num_layers,
             "batch": wl.num_seqs,
             "decode_seqs": wl.num_decode_seqs,
+            "query_tokens": wl.num_tokens,
             "q_heads": wl.num_q_heads,
             "kv_heads": wl.num_kv_heads,
             "head_dim": wl.head_dim,
@@ -334,9 +352,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(wl) if fused else None,
-            "kernel": ("paged decode attention with the decode tokens' append fused in"
-                       if fused else "paged decode attention") +
-                      " (+ split-KV merge when split)",
+            "kernel": kernel,
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
             "measured_copy_gbps": round(copy_gbps, 1),

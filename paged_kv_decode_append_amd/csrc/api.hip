@@ -130,7 +130,8 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
   if (kv_partition_tokens == 0)  // either decode path may run
     plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
   const pkv::PrefillPlan pplan = pkv::plan_prefill(num_seqs - num_decode_seqs, num_q_heads,
-                                                   head_dim, max_context_len, max_query_len);
+                                                   num_kv_heads, head_dim, max_context_len,
+                                                   max_query_len);
   *bytes = workspace_layout(plan, pplan);
   return PKV_OK;
 }
@@ -214,8 +215,9 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
                          kv_partition_tokens == 0 && plan.max_parts > 1;
   if (scheduled && schedule_bytes < splan.schedule_bytes) return PKV_ERR_WORKSPACE;
   if (kv_partition_tokens == 0) plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
-  const pkv::PrefillPlan pplan = pkv::plan_prefill(num_prefill, num_q_heads, cache->head_dim,
-                                                   max_context_len, max_query_len);
+  const pkv::PrefillPlan pplan = pkv::plan_prefill(num_prefill, num_q_heads, cache->num_kv_heads,
+                                                   cache->head_dim, max_context_len,
+                                                   max_query_len);
   const size_t need = workspace_layout(plan, pplan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;

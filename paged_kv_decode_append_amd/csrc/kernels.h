@@ -75,11 +75,13 @@ hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_po
 // `splits` ranges of context tiles, merged by log-sum-exp when splits > 1.
 struct PrefillPlan {
   int32_t splits;
+  bool packed;             // every chunk's G x n rows fit one tile (short chunks)
   int64_t max_row_heads;   // bound on (prefill rows x query heads)
   size_t partial_bytes;
 };
 
-PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t head_dim,
+PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim,
                          int32_t max_context_len, int32_t max_query_len);
 
 // Causal attention of the prefill chunks (sequences first_seq ..

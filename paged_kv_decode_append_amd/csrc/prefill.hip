@@ -26,6 +26,14 @@
 // Tokens past the tile's last row position are zero-filled in LDS, so stale
 // or NaN slots never reach the MFMA accumulators; per-row causal masking is
 // a select to -inf on the scores.
+//
+// Packed rows (PACK): a short chunk -- a few query tokens per sequence, as
+// when a decoding sequence verifies several drafted tokens in one pass --
+// would fill a 64-row tile of one head with a handful of rows and read the
+// same K/V once per query head.  When every chunk has n <= 64 / G tokens,
+// one work-group takes all G heads of one KV group instead: tile row
+// r = k G + hh is query token k of head g G + hh, so each K/V tile leaves
+// HBM once per KV head and the tile holds n G of its 64 rows.
 #include <algorithm>
 #include <climits>
 
@@ -80,7 +88,7 @@ struct TileRegs {
 // needs ~350 registers (one wave per SIMD) and runs slower than HPW = 1 at
 // three waves per SIMD, whose waves hide each other's MFMA, LDS and exp
 // latencies; only HPW = 1 is launched.
-template <int D, int HPW>
+template <int D, int HPW, bool PACK>
 __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGroupsPerCU256) : 1) void prefill_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
     const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
@@ -91,22 +99,28 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   using S = PrefillShape<D>;
   constexpr int KT = S::KT, NT = S::NT, KC = S::KC, DT = S::DT;
   static_assert(KT * (D / 8) == 4 * 256 && (KT / 4) * (D / 8) == 256, "tile split over 256 threads");
+  static_assert(!PACK || HPW == 1, "packed rows carry their own head");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_BYTES / 2];
   __shared__ int64_t s_tile_base[S::kIdTiles * (KT / 16)];  // pool offsets of staged blocks
   uint16_t* k_lds = lds;                         // [KT][KSTRIDE]
   uint16_t* vt_lds = lds + KT * S::KSTRIDE;      // [D][VSTRIDE]
 
   const int i = first_seq + blockIdx.z;
-  const int h0 = blockIdx.y * HPW;               // heads h0 .. h0 + HPW - 1, one KV group
-  const int g = h0 / (num_q_heads / num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  // heads h0 .. h0 + HPW - 1 of one KV group; PACK: all G heads of group y
+  const int h0 = PACK ? blockIdx.y * G : blockIdx.y * HPW;
+  const int g = h0 / G;
   const int split = blockIdx.x % num_splits;
   const int tile_row0 = (blockIdx.x / num_splits) * kRows;  // x past the last tile: exits below
   const int row_base = query_start_loc[i];
   const int n = query_start_loc[i + 1] - row_base;
   const int ctx = min(context_lens[i], ctx_clamp);
-  if (n <= 0 || tile_row0 >= n || ctx < n) return;  // uniform over the work-group
+  const int rows = PACK ? n * G : n;                 // rows of this sequence's row space
+  if (n <= 0 || tile_row0 >= rows || ctx < n) return;  // uniform over the work-group
+  if (PACK && rows > kRows) return;  // a chunk longer than the host hint (broken contract)
   const int p0 = ctx - n;                            // position of the chunk's first row
-  const int pos_hi = p0 + min(tile_row0 + kRows, n) - 1;  // last position this tile needs
+  // last position this tile needs (PACK: the tile holds every token of the chunk)
+  const int pos_hi = PACK ? ctx - 1 : p0 + min(tile_row0 + kRows, n) - 1;
   const int num_kv_tiles = pos_hi / KT + 1;
   const int per_split = (num_kv_tiles + num_splits - 1) / num_splits;
   const int kt_begin = split * per_split;
@@ -114,17 +128,20 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lrow = lane & 15, lgrp = lane >> 4;
-  // This lane's query row (rows past the chunk end reuse the last row; not written).
+  // This lane's query row (rows past the chunk end reuse the last row; not
+  // written): token my_row of the chunk, for heads my_head + hh.
   const int my_row_raw = tile_row0 + 16 * wave + lrow;
-  const bool row_valid = my_row_raw < n;
-  const int my_row = row_valid ? my_row_raw : n - 1;
+  const bool row_valid = my_row_raw < rows;
+  const int my_rr = row_valid ? my_row_raw : rows - 1;
+  const int my_row = PACK ? my_rr / G : my_rr;
+  const int my_head = PACK ? h0 + (my_rr - my_row * G) : h0;
   const int my_pos = p0 + my_row;
 
   // Q^T fragments: B operands, lane = query row lrow, 8 d values per 32-wide chunk.
   f16x8 qb[HPW][KC];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + h0 + hh) * D;
+    const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + my_head + hh) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
       qb[hh][c] = *reinterpret_cast<const f16x8*>(qrow + 32 * c + 8 * lgrp);
@@ -245,7 +262,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     // -inf.  P^T as B operands: chunk c2 covers sub-tiles 2*c2 (elements
     // 0..3) and 2*c2+1 (4..7), converted in pairs; l sums exactly the
     // rounded weights.
-    const bool diagonal = tok0 + KT - 1 > p0 + tile_row0;
+    const bool diagonal = tok0 + KT - 1 > p0 + (PACK ? 0 : tile_row0);
     f16x8 pb[HPW][NT / 2];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const float inv = l_row[hh] > 0.f ? 1.f / l_row[hh] : 0.f;
-    const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + h0 + hh;
+    const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + my_head + hh;
     if (num_splits == 1) {
       uint16_t* dst = out + row_head * D + 4 * lgrp;
 #pragma unroll
@@ -343,7 +360,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     }
     // Partial of this split: (o / l, m, l); l = 0 when no position was visible.
     const int64_t pidx =
-        ((row_base + my_row - first_row) * num_q_heads + h0 + hh) * num_splits + split;
+        ((row_base + my_row - first_row) * num_q_heads + my_head + hh) * num_splits + split;
     float* dst = part_o + pidx * D + 4 * lgrp;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -393,14 +410,17 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
 
 }  // namespace
 
-PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t head_dim,
-                         int32_t max_context_len, int32_t max_query_len) {
+PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t max_context_len, int32_t max_query_len) {
   PrefillPlan plan{};
   plan.splits = 1;
   if (num_prefill_seqs <= 0) return plan;
   const int32_t kt = head_dim == 128 ? PrefillShape<128>::KT : PrefillShape<256>::KT;
+  // every chunk's G n rows fit one tile: one work-group per (sequence, KV head)
+  plan.packed = (int64_t)max_query_len * (num_q_heads / num_kv_heads) <= kRows;
   const int64_t groups =
-      (int64_t)num_prefill_seqs * ((max_query_len + kRows - 1) / kRows) * num_q_heads;
+      plan.packed ? (int64_t)num_prefill_seqs * num_kv_heads
+                  : (int64_t)num_prefill_seqs * ((max_query_len + kRows - 1) / kRows) * num_q_heads;
   const int64_t kv_tiles = (max_context_len + kt - 1) / kt;
   // as many splits as fit in one round of resident work-groups (no tail round)
   const int64_t resident = kCUs * (head_dim == 128 ? kGroupsPerCU128 : kGroupsPerCU256);
@@ -426,19 +446,30 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
       (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o ? part_o + (size_t)plan.max_row_heads * plan.splits * D : nullptr;
-  // x = (query tile, split), padded to a multiple of the 8 XCDs: work-groups
-  // are dealt round-robin over the XCDs, so every head of one (tile, split)
-  // -- in particular the G heads sharing one KV head -- runs on one XCD and
-  // reads the K/V tiles through the same L2.
-  const uint32_t x = ((max_query_len + kRows - 1) / kRows) * plan.splits;
-  const dim3 grid((x + kXcds - 1) / kXcds * kXcds, num_q_heads, num_prefill_seqs);
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, 1>), grid, dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                     static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
-                     num_q_heads, block_tables, max_blocks_per_seq, context_lens,
-                     query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
-                     static_cast<uint16_t*>(out), part_o, part_ml);
+  if (plan.packed) {
+    // x = split, y = KV head: each work-group holds all heads of its group
+    const dim3 grid((uint32_t)plan.splits, num_kv_heads, num_prefill_seqs);
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, true>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                       query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
+                       static_cast<uint16_t*>(out), part_o, part_ml);
+  } else {
+    // x = (query tile, split), padded to a multiple of the 8 XCDs: work-groups
+    // are dealt round-robin over the XCDs, so every head of one (tile, split)
+    // -- in particular the G heads sharing one KV head -- runs on one XCD and
+    // reads the K/V tiles through the same L2.
+    const uint32_t x = ((max_query_len + kRows - 1) / kRows) * plan.splits;
+    const dim3 grid((x + kXcds - 1) / kXcds * kXcds, num_q_heads, num_prefill_seqs);
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, false>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
+                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+                       num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                       query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
+                       static_cast<uint16_t*>(out), part_o, part_ml);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return err;
   const int64_t waves = plan.max_row_heads;

@@ -35,6 +35,8 @@ Workload recipes (the five shapes the benchmark and parity tests use):
   qwen_mixed      28 layers, 64 decode sequences with ctx uniform on
                   [256, 4096] plus one prefill chunk of 512 query tokens on an
                   8,192-token cached prefix (ctx 8,704).
+  qwen_spec       28 layers, 64 sequences with ctx uniform on [256, 4096],
+                  each verifying 4 query tokens (multi-token decode).
 """
 from __future__ import annotations
 
@@ -129,6 +131,13 @@ class Workload:
         pairs = int((n * (ctx - n + 1) + n * (n - 1) // 2).sum())
         return 4 * self.head_dim * self.num_q_heads * pairs
 
+    def short_chunk(self) -> np.ndarray:
+        """bool [B]: sequences whose new tokens, times the query heads per KV
+        head, fit one 64-row tile (decodes and multi-token decodes): their
+        attention streams the cache rather than filling the matrix cores."""
+        g = self.num_q_heads // self.num_kv_heads
+        return self.new_tokens.astype(np.int64) * g <= 64
+
     def append_bytes_per_layer(self) -> int:
         return 2 * self.num_tokens * self.num_kv_heads * self.head_dim * FP16_BYTES
 
@@ -191,6 +200,19 @@ def qwen_mixed(seed: int = 0, decodes: int = 64, chunk: int = 512, prefix: int =
     return _build("qwen_mixed", layers, 12, 2, 128, ctx, new, decodes, 1.2, seed)
 
 
+def qwen_spec(seed: int = 0, batch: int = 64, query_len: int = 4, layers: int = 28) -> Workload:
+    """Decoding sequences that each verify several tokens in one pass: the
+    token sampled last pass plus query_len - 1 drafted ones (a request's
+    scheduled tokens include its speculative ones -- deepconcepts.dev,
+    "Continuous Batching Is Not a Bigger Batch", scheduler note on
+    num_tokens_with_spec).  Contexts uniform on [256, 4096] after the step,
+    as the decodes of qwen_mixed; every sequence is a short causal chunk."""
+    rng = np.random.default_rng(seed + 3)
+    ctx = rng.integers(256, 4096, size=batch, endpoint=True).astype(np.int32)
+    new = np.full(batch, query_len, dtype=np.int32)
+    return _build("qwen_spec", layers, 12, 2, 128, ctx, new, 0, 1.2, seed)
+
+
 def custom(name: str, ctx, new, num_decode_seqs: int, hq: int, hkv: int, d: int, layers: int = 1,
            pool_factor: float = 1.5, seed: int = 0, pool_blocks: int | None = None) -> Workload:
     """Arbitrary small shapes for parity and edge-case tests."""
@@ -204,6 +226,7 @@ WORKLOADS = {
     "qwen_ragged": qwen_ragged,
     "long_context": long_context,
     "qwen_mixed": qwen_mixed,
+    "qwen_spec": qwen_spec,
 }
 
 
