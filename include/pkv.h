@@ -149,8 +149,9 @@ int pkv_kv_append(const pkv_kv_cache* cache, const void* k_new, const void* v_ne
  *   max_context_len             >= every ctx_i
  *   max_query_len               >= every n_i (1 for a pure decode step)
  *   kv_partition_tokens         0 = automatic; otherwise force this many
- *                               context tokens per split-KV partition
- *                               (multiple of 64)
+ *                               context tokens per split-KV partition of
+ *                               the decode sequences and of packed short
+ *                               chunks (multiple of 64)
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED.
  */
 int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
@@ -229,11 +230,15 @@ int pkv_decode_schedule(const int32_t* context_lens, int32_t num_decode_seqs,
  *   workspace        device buffer of at least the size that
  *                    pkv_attention_workspace_size reports (may be NULL when
  *                    that size is 0); contents need not be initialised and
- *                    are undefined afterwards
+ *                    are undefined afterwards.  Calls that share one
+ *                    workspace must be ordered on one stream.
  * Launches: the decode kernel (grid over sequence x KV head x partition, or
  * one work-group per schedule share), the log-sum-exp merge of partitions or
  * pieces when any context is split, and the MFMA prefill kernel (+ its merge)
- * when prefill chunks are present; all on `stream`.
+ * when prefill chunks are present -- short chunks (max_query_len x
+ * num_q_heads / num_kv_heads <= 64, e.g. a decoding sequence verifying a few
+ * drafted tokens) with all query heads of a KV head packed into one
+ * work-group; all on `stream`.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
  * PKV_ERR_HIP.
  */

@@ -131,7 +131,7 @@ int pkv_attention_workspace_size(int32_t num_seqs, int32_t num_decode_seqs,
     plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
   const pkv::PrefillPlan pplan = pkv::plan_prefill(num_seqs - num_decode_seqs, num_q_heads,
                                                    num_kv_heads, head_dim, max_context_len,
-                                                   max_query_len);
+                                                   max_query_len, kv_partition_tokens);
   *bytes = workspace_layout(plan, pplan);
   return PKV_OK;
 }
@@ -217,7 +217,7 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
   if (kv_partition_tokens == 0) plan.partial_bytes = std::max(plan.partial_bytes, splan.partial_bytes);
   const pkv::PrefillPlan pplan = pkv::plan_prefill(num_prefill, num_q_heads, cache->num_kv_heads,
                                                    cache->head_dim, max_context_len,
-                                                   max_query_len);
+                                                   max_query_len, kv_partition_tokens);
   const size_t need = workspace_layout(plan, pplan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;

@@ -76,13 +76,14 @@ hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_po
 struct PrefillPlan {
   int32_t splits;
   bool packed;             // every chunk's G x n rows fit one tile (short chunks)
+  int32_t split_tiles;     // KV tiles per split (packed; 0: even ranges of the context)
   int64_t max_row_heads;   // bound on (prefill rows x query heads)
   size_t partial_bytes;
 };
 
 PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim,
-                         int32_t max_context_len, int32_t max_query_len);
+                         int32_t head_dim, int32_t max_context_len, int32_t max_query_len,
+                         int32_t kv_partition_tokens);
 
 // Causal attention of the prefill chunks (sequences first_seq ..
 // first_seq + num_prefill_seqs - 1) on the matrix cores.

@@ -54,6 +54,7 @@ constexpr int64_t kGroupsPerCU128 = 3;
 constexpr int64_t kGroupsPerCU256 = 2;
 constexpr uint32_t kXcds = 8;
 constexpr int64_t kMaxPrefillSplits = 16;
+constexpr int64_t kPackedRounds = 2;  // packed rows: target rounds of resident work-groups
 constexpr float kRescaleSlack = 8.f;  // lazy max (base 2): rescale only past m + 8
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -94,7 +95,8 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
     int32_t num_q_heads, const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
-    int32_t first_seq, int32_t ctx_clamp, int32_t num_splits, float scale_log2,
+    int32_t first_seq, int32_t ctx_clamp, int32_t num_splits, int32_t split_tiles,
+    float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
   using S = PrefillShape<D>;
   constexpr int KT = S::KT, NT = S::NT, KC = S::KC, DT = S::DT;
@@ -110,7 +112,10 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   // heads h0 .. h0 + HPW - 1 of one KV group; PACK: all G heads of group y
   const int h0 = PACK ? blockIdx.y * G : blockIdx.y * HPW;
   const int g = h0 / G;
-  const int split = blockIdx.x % num_splits;
+  // PACK: the highest split first -- only long contexts have high splits, so
+  // the longest work starts first and short sequences fill in behind it
+  const int split = PACK ? num_splits - 1 - (int)(blockIdx.x % num_splits)
+                         : (int)(blockIdx.x % num_splits);
   const int tile_row0 = (blockIdx.x / num_splits) * kRows;  // x past the last tile: exits below
   const int row_base = query_start_loc[i];
   const int n = query_start_loc[i + 1] - row_base;
@@ -122,7 +127,10 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   // last position this tile needs (PACK: the tile holds every token of the chunk)
   const int pos_hi = PACK ? ctx - 1 : p0 + min(tile_row0 + kRows, n) - 1;
   const int num_kv_tiles = pos_hi / KT + 1;
-  const int per_split = (num_kv_tiles + num_splits - 1) / num_splits;
+  // KV tiles per split: a fixed count (split_tiles > 0: short sequences use
+  // fewer splits), or the context cut into num_splits even ranges
+  const int per_split =
+      split_tiles > 0 ? split_tiles : (num_kv_tiles + num_splits - 1) / num_splits;
   const int kt_begin = split * per_split;
   const int kt_end = min(kt_begin + per_split, num_kv_tiles);
 
@@ -136,6 +144,21 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   const int my_row = PACK ? my_rr / G : my_rr;
   const int my_head = PACK ? h0 + (my_rr - my_row * G) : h0;
   const int my_pos = p0 + my_row;
+  if (kt_begin >= kt_end) {
+    // an empty split (short context, fixed tiles per split): the merge reads
+    // only its weight l = 0
+    if (row_valid && lgrp == 0) {
+      const int64_t first_row = query_start_loc[first_seq];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const int64_t pidx =
+            ((row_base + my_row - first_row) * num_q_heads + my_head + hh) * num_splits + split;
+        part_ml[pidx * 2] = -__builtin_huge_valf();
+        part_ml[pidx * 2 + 1] = 0.f;
+      }
+    }
+    return;  // uniform over the work-group
+  }
 
   // Q^T fragments: B operands, lane = query row lrow, 8 d values per 32-wide chunk.
   f16x8 qb[HPW][KC];
@@ -375,32 +398,50 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 // Merge of the splits of every (prefill row, query head): one wave each.
 //   M = max m_s over splits with l_s > 0, w_s = l_s 2^(m_s - M),
 //   O = sum_s w_s o_s / sum_s w_s.
+// Lane s holds split s's (m, l), so the weights take one round of loads and
+// two wave reductions; every split's o is then requested at once (a split
+// that saw no position -- l = 0 -- may have left o unwritten: its value is
+// read but selected away, never multiplied).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ query_start_loc, int32_t first_seq, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_splits, int64_t max_row_heads, uint16_t* __restrict__ out) {
   constexpr int EPL = D / 64;
+  static_assert(kMaxPrefillSplits <= 64, "one lane per split");
   const int lane = threadIdx.x & 63;
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t first_row = query_start_loc[first_seq];
   const int64_t rows = (int64_t)query_start_loc[num_seqs] - first_row;
   if (rh >= rows * num_q_heads || rh >= max_row_heads) return;
   const float* ml = part_ml + rh * num_splits * 2;
-  float M = -__builtin_huge_valf();
-  for (int s = 0; s < num_splits; ++s)
-    if (ml[2 * s + 1] > 0.f) M = fmaxf(M, ml[2 * s]);
-  float W = 0.f, acc[EPL];
+  float m = -__builtin_huge_valf(), l = 0.f;
+  if (lane < num_splits) {
+    m = ml[2 * lane];
+    l = ml[2 * lane + 1];
+  }
+  float M = l > 0.f ? m : -__builtin_huge_valf();
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float w = l > 0.f ? l * fast_exp2(m - M) : 0.f;
+  float W = w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
+  float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int s = 0; s < num_splits; ++s) {
-    const float l = ml[2 * s + 1];
-    if (!(l > 0.f)) continue;
-    const float w = l * fast_exp2(ml[2 * s] - M);
-    W += w;
-    const float* src = part_o + (rh * num_splits + s) * D + EPL * lane;
+  const float* src = part_o + rh * num_splits * D + EPL * lane;
+  // loads of splits past num_splits re-read the last one (in bounds, always
+  // issued, so that all loads are in flight together) and get weight 0
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * src[e];
+  for (int s = 0; s < kMaxPrefillSplits; ++s) {
+    const int sc = min(s, num_splits - 1);
+    const float ws = s < num_splits ? __shfl(w, s) : 0.f;
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = src[(int64_t)sc * D + e];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += ws > 0.f ? ws * o[e] : 0.f;
   }
   uint16_t* dst = out + (first_row * num_q_heads + rh) * D + EPL * lane;
   const float inv = W > 0.f ? 1.f / W : 0.f;
@@ -411,7 +452,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
 }  // namespace
 
 PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t max_context_len, int32_t max_query_len) {
+                         int32_t head_dim, int32_t max_context_len, int32_t max_query_len,
+                         int32_t kv_partition_tokens) {
   PrefillPlan plan{};
   plan.splits = 1;
   if (num_prefill_seqs <= 0) return plan;
@@ -422,11 +464,25 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
       plan.packed ? (int64_t)num_prefill_seqs * num_kv_heads
                   : (int64_t)num_prefill_seqs * ((max_query_len + kRows - 1) / kRows) * num_q_heads;
   const int64_t kv_tiles = (max_context_len + kt - 1) / kt;
-  // as many splits as fit in one round of resident work-groups (no tail round)
   const int64_t resident = kCUs * (head_dim == 128 ? kGroupsPerCU128 : kGroupsPerCU256);
-  int64_t splits = resident / groups;
-  splits = std::min<int64_t>(std::min<int64_t>(splits, kMaxPrefillSplits), kv_tiles);
-  plan.splits = (int32_t)std::max<int64_t>(splits, 1);
+  if (plan.packed) {
+    // A fixed number of KV tiles per split, so that a long context gets more
+    // splits than a short one: about kPackedRounds rounds of resident
+    // work-groups if every context had the longest length.
+    int64_t per = kv_partition_tokens > 0
+                      ? std::max<int64_t>(1, kv_partition_tokens / kt)
+                      : (groups * kv_tiles + kPackedRounds * resident - 1) / (kPackedRounds * resident);
+    per = std::max<int64_t>(std::max<int64_t>(per, 1),
+                            (kv_tiles + kMaxPrefillSplits - 1) / kMaxPrefillSplits);
+    plan.splits = (int32_t)((kv_tiles + per - 1) / per);
+    plan.split_tiles = plan.splits > 1 ? (int32_t)per : 0;
+  } else {
+    // as many splits as fit in one round of resident work-groups (no tail round)
+    int64_t splits = resident / groups;
+    splits = std::min<int64_t>(std::min<int64_t>(splits, kMaxPrefillSplits), kv_tiles);
+    plan.splits = (int32_t)std::max<int64_t>(splits, 1);
+    plan.split_tiles = 0;
+  }
   plan.max_row_heads = (int64_t)num_prefill_seqs * max_query_len * num_q_heads;
   plan.partial_bytes =
       plan.splits > 1 ? (size_t)plan.max_row_heads * plan.splits * (head_dim + 2) * sizeof(float)
@@ -454,7 +510,8 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                        static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
                        num_q_heads, block_tables, max_blocks_per_seq, context_lens,
-                       query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
+                       query_start_loc, first_seq, ctx_clamp, plan.splits, plan.split_tiles,
+                       scale * kLog2e,
                        static_cast<uint16_t*>(out), part_o, part_ml);
   } else {
     // x = (query tile, split), padded to a multiple of the 8 XCDs: work-groups
@@ -467,7 +524,8 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
                        static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
                        num_q_heads, block_tables, max_blocks_per_seq, context_lens,
-                       query_start_loc, first_seq, ctx_clamp, plan.splits, scale * kLog2e,
+                       query_start_loc, first_seq, ctx_clamp, plan.splits, plan.split_tiles,
+                       scale * kLog2e,
                        static_cast<uint16_t*>(out), part_o, part_ml);
   }
   hipError_t err = hipGetLastError();
