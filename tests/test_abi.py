@@ -12,12 +12,14 @@ import paged_kv_decode_append_amd as pkv
 import oracle
 import workloads
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "pkv.h")
+SCHED_HEADER = os.path.join(INCLUDE, "pkv_sched.h")
 FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below fails validation first
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"\b(pkv_\w+)\s*\(", text))
 
@@ -27,6 +29,15 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(pkv.EXPORTED)
     for name in declared:
         assert hasattr(pkv.lib, name), name
+
+
+def test_every_scheduler_symbol_is_exported():
+    from paged_kv_decode_append_amd.scheduler import SCHED_EXPORTED
+    declared = _declared(SCHED_HEADER)
+    assert declared == set(SCHED_EXPORTED)
+    for name in declared:
+        assert hasattr(pkv.lib, name), name
+    assert set(os.listdir(INCLUDE)) == {"pkv.h", "pkv_sched.h"}
 
 
 def test_version_and_status_strings():

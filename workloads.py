@@ -220,6 +220,45 @@ def custom(name: str, ctx, new, num_decode_seqs: int, hq: int, hkv: int, d: int,
                   pool_blocks=pool_blocks)
 
 
+def serving_requests(seed: int = 0, num_requests: int = 256, prompt_range=(256, 2480),
+                     output_range=(50, 781), shared_prefix: int = 0, prefix_groups: int = 0):
+    """A queue of requests for the per-pass scheduler: prompt lengths uniform
+    on prompt_range (mean 1,368 by default, the prompt size of the pages'
+    worked example -- deepconcepts.dev, "Where the batch size actually comes
+    from"), output lengths uniform on output_range (the 50- and 781-token
+    requests of the same page's introduction).  With prefix_groups > 0 each
+    request draws a group whose first shared_prefix prompt tokens it shares.
+    Returns (prompt_lens, max_new_tokens, prefix_ids) int arrays."""
+    rng = np.random.default_rng(seed + 4)
+    prompts = rng.integers(prompt_range[0], prompt_range[1], size=num_requests, endpoint=True)
+    outputs = rng.integers(output_range[0], output_range[1], size=num_requests, endpoint=True)
+    if prefix_groups > 0:
+        groups = rng.integers(0, prefix_groups, size=num_requests)
+        prompts = np.maximum(prompts, shared_prefix + 1)
+    else:
+        groups = np.full(num_requests, -1)
+    return prompts.astype(np.int64), outputs.astype(np.int64), groups.astype(np.int64)
+
+
+def free_block_order(num_blocks: int, seed: int = 0) -> np.ndarray:
+    """A seeded permutation of the pool: the initial order of the scheduler's
+    free-block queue, so that block tables scatter through the pool."""
+    return np.random.default_rng(seed + 5).permutation(num_blocks).astype(np.int32)
+
+
+def token_kv_rows(key: int, positions, num_kv_heads: int, head_dim: int, layer: int = 0,
+                  seed: int = 0) -> np.ndarray:
+    """Deterministic N(0,1) fp16 K and V rows of tokens, a pure function of
+    (key, position, layer): float16 [len(positions), 2, Hkv, d] (0 = K, 1 = V).
+    A token that is computed again (after a preemption), or shared by
+    requests with a common prefix (same key), gets the same rows."""
+    out = np.empty((len(positions), 2, num_kv_heads, head_dim), np.float16)
+    for j, p in enumerate(positions):
+        rng = np.random.default_rng([seed, int(key) & 0x7FFFFFFFFFFFFFFF, int(p), layer])
+        out[j] = rng.standard_normal((2, num_kv_heads, head_dim)).astype(np.float16)
+    return out
+
+
 WORKLOADS = {
     "small_b4": small_b4,
     "qwen_uniform": qwen_uniform,
