@@ -8,8 +8,10 @@ imports this package.  It shares no code with the HIP kernels: the C part
 knows nothing of block tables.
 
 Functions (each cites what it follows in the C source):
-  slot_mapping, kv_append, paged_attention, attention_partial, lse_merge,
-  half_to_float64.
+  slot_mapping, kv_append, paged_attention, paged_attention_fp8,
+  attention_partial, lse_merge, half_to_float64.
+Submodules: ``fp8`` (E4M3 codes and the per-row quantization of an fp8
+cache), ``scheduler`` (plain model of the per-pass scheduler), ``dense``.
 """
 from __future__ import annotations
 
@@ -51,6 +53,8 @@ def _load():
     lib.oracle_kv_append.argtypes = [P, P, i64, i32, i32, i32, P, P, P, i32]
     lib.oracle_paged_attention.argtypes = [P, P, P, i64, i32, i32, i32, P, i32, P, P, i32,
                                            i32, f64, P, P, P, i32]
+    lib.oracle_paged_attention_f64.argtypes = [P, P, P, i64, i32, i32, i32, P, i32, P, P, i32,
+                                               i32, f64, P, P, i32]
     lib.oracle_attention_partial.argtypes = [P, P, P, i32, i32, i32, f64, P, P, P]
     lib.oracle_lse_merge.argtypes = [P, P, P, i32, i32, P]
     lib.oracle_attention_contiguous.argtypes = [P, P, P, i32, i32, f64, P]
@@ -146,6 +150,30 @@ def paged_attention(q, k_pool, v_pool, block_tables, context_lens, query_start_l
         0 if sub is None else sub.shape[0])
     _check(rc, "oracle_paged_attention")
     return (out, lse) if want_lse else out
+
+
+def paged_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                        query_start_loc, scale: float, seq_subset=None):
+    """fp64 attention [T, Hq, d] over an fp8 cache: the pools are dequantized
+    (oracle.fp8.dequantize, exact) and attended as in paged_attention."""
+    from . import fp8
+    qb = _bits(q)
+    kd = np.ascontiguousarray(fp8.dequantize(k_codes, k_scales))
+    vd = np.ascontiguousarray(fp8.dequantize(v_codes, v_scales))
+    bt = _c(block_tables, np.int32)
+    ctx = _c(context_lens, np.int32)
+    qsl = None if query_start_loc is None else _c(query_start_loc, np.int32)
+    T, Hq, d = qb.shape
+    NB, Hkv, bs, d2 = kd.shape
+    assert d2 == d
+    out = np.full((T, Hq, d), np.nan, dtype=np.float64)
+    sub = None if seq_subset is None else _c(seq_subset, np.int32)
+    rc = _load().oracle_paged_attention_f64(
+        _ptr(qb), _ptr(kd), _ptr(vd), NB, Hkv, bs, d, _ptr(bt), bt.shape[1], _ptr(ctx),
+        _ptr(qsl), ctx.shape[0], Hq, float(scale), _ptr(out), _ptr(sub),
+        0 if sub is None else sub.shape[0])
+    _check(rc, "oracle_paged_attention_f64")
+    return out
 
 
 def attention_partial(q, K, V, lo: int, hi: int, scale: float):

@@ -161,11 +161,13 @@ int oracle_kv_append(uint16_t* k_pool, uint16_t* v_pool, int64_t num_blocks,
  * Gather: copy the rows of positions [0, count) of KV head g of sequence i
  * from the pool into a contiguous [count][head_dim] fp64 array, following
  * the block table (position p is in block table entry p / block_size, at
- * offset p % block_size).
+ * offset p % block_size).  The pool is fp16 bits (pool) or, for a quantized
+ * cache already dequantized, fp64 values (pool64); exactly one is non-NULL.
  */
-static int gather_rows(const uint16_t* pool, int64_t num_blocks, int32_t num_kv_heads,
-                       int32_t block_size, int32_t head_dim, const int32_t* table_row,
-                       int32_t max_blocks_per_seq, int32_t g, int32_t count, double* out) {
+static int gather_rows(const uint16_t* pool, const double* pool64, int64_t num_blocks,
+                       int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                       const int32_t* table_row, int32_t max_blocks_per_seq, int32_t g,
+                       int32_t count, double* out) {
   for (int32_t p = 0; p < count; ++p) {
     int32_t logical_block = p / block_size;
     if (logical_block >= max_blocks_per_seq) return ORACLE_ERR_RANGE;
@@ -173,7 +175,8 @@ static int gather_rows(const uint16_t* pool, int64_t num_blocks, int32_t num_kv_
     if (block < 0 || block >= num_blocks) return ORACLE_ERR_RANGE;
     int64_t base = ((block * num_kv_heads + g) * block_size + p % block_size) * head_dim;
     for (int32_t e = 0; e < head_dim; ++e)
-      out[(int64_t)p * head_dim + e] = oracle_half_to_double(pool[base + e]);
+      out[(int64_t)p * head_dim + e] =
+          pool ? oracle_half_to_double(pool[base + e]) : pool64[base + e];
   }
   return ORACLE_OK;
 }
@@ -223,14 +226,17 @@ static void attend_range(const double* q, const double* K, const double* V, int3
  * [0, ctx - n + k] (decode: n = 1, the whole context including the token
  * just appended).
  */
-int oracle_paged_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                           int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
-                           int32_t head_dim, const int32_t* block_tables,
-                           int32_t max_blocks_per_seq, const int32_t* context_lens,
-                           const int32_t* query_start_loc, int32_t num_seqs,
-                           int32_t num_q_heads, double scale, double* out, double* lse_out,
-                           const int32_t* seq_subset, int32_t num_subset) {
-  if (!q || !k_pool || !v_pool || !block_tables || !context_lens || !out)
+static int paged_attention_impl(const uint16_t* q, const uint16_t* k_pool,
+                                const uint16_t* v_pool, const double* k_pool64,
+                                const double* v_pool64, int64_t num_blocks,
+                                int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t num_q_heads, double scale,
+                                double* out, double* lse_out, const int32_t* seq_subset,
+                                int32_t num_subset) {
+  if (!q || !(k_pool || k_pool64) || !(v_pool || v_pool64) || !block_tables || !context_lens ||
+      !out)
     return ORACLE_ERR_ARG;
   if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
       head_dim <= 0 || block_size <= 0)
@@ -266,10 +272,10 @@ int oracle_paged_attention(const uint16_t* q, const uint16_t* k_pool, const uint
       continue;
     }
     const int32_t* row = block_tables + (int64_t)i * max_blocks_per_seq;
-    int rc = gather_rows(k_pool, num_blocks, num_kv_heads, block_size, head_dim, row,
+    int rc = gather_rows(k_pool, k_pool64, num_blocks, num_kv_heads, block_size, head_dim, row,
                          max_blocks_per_seq, g, ctx, K);
     if (rc == ORACLE_OK)
-      rc = gather_rows(v_pool, num_blocks, num_kv_heads, block_size, head_dim, row,
+      rc = gather_rows(v_pool, v_pool64, num_blocks, num_kv_heads, block_size, head_dim, row,
                        max_blocks_per_seq, g, ctx, V);
     if (rc != ORACLE_OK) {
 #pragma omp atomic write
@@ -291,6 +297,40 @@ int oracle_paged_attention(const uint16_t* q, const uint16_t* k_pool, const uint
     free(K); free(V); free(qd); free(s);
   }
   return status;
+}
+
+int oracle_paged_attention(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                           int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                           int32_t head_dim, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int32_t num_q_heads, double scale, double* out, double* lse_out,
+                           const int32_t* seq_subset, int32_t num_subset) {
+  if (!k_pool || !v_pool) return ORACLE_ERR_ARG;
+  return paged_attention_impl(q, k_pool, v_pool, NULL, NULL, num_blocks, num_kv_heads,
+                              block_size, head_dim, block_tables, max_blocks_per_seq,
+                              context_lens, query_start_loc, num_seqs, num_q_heads, scale, out,
+                              lse_out, seq_subset, num_subset);
+}
+
+/*
+ * The same over pools of fp64 values [num_blocks][num_kv_heads][block_size]
+ * [head_dim]: a quantized (fp8) cache after dequantization (code value x
+ * row scale, exact in fp64), so that attention over it is the plain
+ * definition again.
+ */
+int oracle_paged_attention_f64(const uint16_t* q, const double* k_pool, const double* v_pool,
+                               int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                               int32_t head_dim, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs,
+                               int32_t num_q_heads, double scale, double* out,
+                               const int32_t* seq_subset, int32_t num_subset) {
+  if (!k_pool || !v_pool) return ORACLE_ERR_ARG;
+  return paged_attention_impl(q, NULL, NULL, k_pool, v_pool, num_blocks, num_kv_heads,
+                              block_size, head_dim, block_tables, max_blocks_per_seq,
+                              context_lens, query_start_loc, num_seqs, num_q_heads, scale, out,
+                              NULL, seq_subset, num_subset);
 }
 
 /*
