@@ -67,12 +67,29 @@ typedef enum {
   PKV_ERR_CONTRACT = -5     /* pkv_validate_step found a device-content violation  */
 } pkv_status;
 
+/* Element type of a KV cache (pkv_kv_cache.kv_dtype). */
+enum {
+  PKV_KV_FP16 = 0,     /* IEEE binary16 values */
+  PKV_KV_FP8_E4M3 = 1  /* 8-bit codes + one fp32 scale per (token, KV head) row */
+};
+
 /*
- * One layer's paged KV cache.  k_pool and v_pool are device fp16 arrays of
- * shape [num_blocks][num_kv_heads][block_size][head_dim]: one block of one
- * KV head is block_size * head_dim contiguous values (4 KiB at d = 128).
+ * One layer's paged KV cache.  k_pool and v_pool are device arrays of shape
+ * [num_blocks][num_kv_heads][block_size][head_dim]: one block of one KV head
+ * is block_size * head_dim contiguous values (4 KiB at d = 128 in fp16).
  * Physical block b of KV head g holds the rows of block_size consecutive
  * token positions of whichever sequence owns b.  Owned by the caller.
+ *
+ * kv_dtype PKV_KV_FP8_E4M3 (a quantized cache: 8-bit KV halves the bytes of
+ * a window, "before scales" -- a8q9.cn, "An advertised batch limit proves
+ * nothing until sampled"): the pools hold OCP FP8 E4M3 codes (1 byte per
+ * value: sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+ * 448), and k_scale / v_scale are device fp32 arrays [num_blocks]
+ * [num_kv_heads][block_size]: row (b, g, o) stands for code value x
+ * scale[b][g][o].  pkv_kv_append writes each new row with the smallest
+ * power-of-two scale 2^e such that max|x| <= 448 x 2^e (1 for a zero row)
+ * and codes x / 2^e rounded to nearest, ties to even.  For fp16 caches
+ * kv_dtype is 0 and the scale pointers are ignored.
  */
 typedef struct {
   void* k_pool;
@@ -81,6 +98,9 @@ typedef struct {
   int32_t block_size;   /* must be 16 */
   int32_t num_kv_heads; /* >= 1 */
   int32_t head_dim;     /* 128 or 256 */
+  int32_t kv_dtype;     /* PKV_KV_FP16 or PKV_KV_FP8_E4M3 */
+  void* k_scale;        /* fp8: fp32 [num_blocks][num_kv_heads][block_size] */
+  void* v_scale;
 } pkv_kv_cache;
 
 /* Library version (PKV_VERSION of the build). */

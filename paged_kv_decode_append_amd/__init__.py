@@ -46,10 +46,16 @@ class PkvError(RuntimeError):
         self.status = status
 
 
+PKV_KV_FP16 = 0
+PKV_KV_FP8_E4M3 = 1
+
+
 class _Cache(ctypes.Structure):
     _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
                 ("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
-                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p)]
 
 
 def _load():
@@ -137,17 +143,35 @@ def _need(t, dtype, name):
 
 
 class KVCache:
-    """One layer's pools: k_pool, v_pool fp16 [num_blocks, num_kv_heads, 16, head_dim]."""
+    """One layer's pools: k_pool, v_pool [num_blocks, num_kv_heads, 16, head_dim],
+    fp16 values, or (with k_scale / v_scale fp32 [num_blocks, num_kv_heads, 16])
+    uint8 fp8-E4M3 codes of a quantized cache."""
 
-    def __init__(self, k_pool, v_pool):
+    def __init__(self, k_pool, v_pool, k_scale=None, v_scale=None):
         import torch
-        _need(k_pool, torch.float16, "k_pool")
-        _need(v_pool, torch.float16, "v_pool")
+        fp8 = k_scale is not None or v_scale is not None
+        dt = torch.uint8 if fp8 else torch.float16
+        _need(k_pool, dt, "k_pool")
+        _need(v_pool, dt, "v_pool")
         if k_pool.shape != v_pool.shape or k_pool.dim() != 4:
             raise ValueError("k_pool and v_pool must share a 4-d shape")
         self.k_pool, self.v_pool = k_pool, v_pool
         nb, hkv, bs, d = k_pool.shape
-        self._c = _Cache(k_pool.data_ptr(), v_pool.data_ptr(), nb, bs, hkv, d)
+        self.k_scale, self.v_scale = k_scale, v_scale
+        if fp8:
+            _need(k_scale, torch.float32, "k_scale")
+            _need(v_scale, torch.float32, "v_scale")
+            if tuple(k_scale.shape) != (nb, hkv, bs) or tuple(v_scale.shape) != (nb, hkv, bs):
+                raise ValueError("scales must be [num_blocks, num_kv_heads, block_size]")
+            self._c = _Cache(k_pool.data_ptr(), v_pool.data_ptr(), nb, bs, hkv, d,
+                             PKV_KV_FP8_E4M3, k_scale.data_ptr(), v_scale.data_ptr())
+        else:
+            self._c = _Cache(k_pool.data_ptr(), v_pool.data_ptr(), nb, bs, hkv, d,
+                             PKV_KV_FP16, None, None)
+
+    @property
+    def is_fp8(self):
+        return self._c.kv_dtype == PKV_KV_FP8_E4M3
 
     @property
     def num_blocks(self):

@@ -24,6 +24,10 @@ bool supported_head_dim(int32_t d) { return d == 128 || d == 256; }
 
 int check_cache(const pkv_kv_cache* cache) {
   if (!cache || !cache->k_pool || !cache->v_pool) return PKV_ERR_INVALID_ARG;
+  if (cache->kv_dtype != PKV_KV_FP16 && cache->kv_dtype != PKV_KV_FP8_E4M3)
+    return PKV_ERR_UNSUPPORTED;
+  if (cache->kv_dtype == PKV_KV_FP8_E4M3 && (!cache->k_scale || !cache->v_scale))
+    return PKV_ERR_INVALID_ARG;
   if (cache->num_blocks <= 0 || cache->num_kv_heads <= 0) return PKV_ERR_INVALID_ARG;
   if (cache->block_size != kBlockSize) return PKV_ERR_UNSUPPORTED;
   if (!supported_head_dim(cache->head_dim)) return PKV_ERR_UNSUPPORTED;
@@ -107,6 +111,12 @@ int pkv_kv_append(const pkv_kv_cache* cache, const void* k_new, const void* v_ne
   if (num_tokens < 0) return PKV_ERR_INVALID_ARG;
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (cache->kv_dtype == PKV_KV_FP8_E4M3)
+    return from_hip(pkv::launch_kv_append_fp8(
+        cache->k_pool, cache->v_pool, static_cast<float*>(cache->k_scale),
+        static_cast<float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
+        cache->head_dim, k_new, v_new, slot_mapping, num_tokens,
+        static_cast<hipStream_t>(stream)));
   return from_hip(pkv::launch_kv_append(cache->k_pool, cache->v_pool, cache->num_blocks,
                                         cache->num_kv_heads, cache->head_dim, k_new, v_new,
                                         slot_mapping, num_tokens,
@@ -222,6 +232,23 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
+    // quantized cache: decode sequences only; the step's rows are appended
+    // (quantized) by the append kernel, then the decode kernel reads codes
+    if (num_prefill > 0) return PKV_ERR_UNSUPPORTED;
+    if (fused) {
+      rc = from_hip(pkv::launch_kv_append_fp8(
+          cache->k_pool, cache->v_pool, static_cast<float*>(cache->k_scale),
+          static_cast<float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
+          cache->head_dim, k_new, v_new, slot_mapping, num_tokens, s));
+      if (rc != PKV_OK) return rc;
+    }
+    return from_hip(pkv::launch_paged_decode_fp8(
+        q, cache->k_pool, cache->v_pool, static_cast<const float*>(cache->k_scale),
+        static_cast<const float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
+        num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq, context_lens,
+        num_decode_seqs, scale, plan, out, workspace, s));
+  }
   if (fused && num_tokens > num_decode_seqs) {
     // rows of the prefill chunks follow the decode rows
     const size_t row_bytes = (size_t)cache->num_kv_heads * cache->head_dim * 2;

@@ -370,11 +370,8 @@ hipError_t launch_decode_dga(const void* q, void* k_pool, void* v_pool, int64_t 
                      static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
-  const int32_t rows = num_decode_seqs * num_q_heads;
-  hipLaunchKernelGGL((lse_merge_kernel<D>), dim3(rows), dim3(256), 0, stream, part_o, part_ml,
-                     context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts, num_q_heads,
-                     static_cast<uint16_t*>(out));
-  return hipGetLastError();
+  return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
+                             num_q_heads, D, out, stream);
 }
 
 template <int D>
@@ -401,6 +398,26 @@ hipError_t launch_decode_d(int32_t group, const void* q, void* k_pool, void* v_p
 }
 
 }  // namespace
+
+hipError_t launch_decode_merge(const float* part_o, const float* part_ml,
+                               const int32_t* context_lens, int32_t ctx_clamp,
+                               const DecodePlan& plan, int32_t num_decode_seqs,
+                               int32_t num_q_heads, int32_t head_dim, void* out,
+                               hipStream_t stream) {
+  const int32_t rows = num_decode_seqs * num_q_heads;
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  if (head_dim == 128)
+    hipLaunchKernelGGL((lse_merge_kernel<128>), dim3(rows), dim3(256), 0, stream, part_o,
+                       part_ml, context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts,
+                       num_q_heads, static_cast<uint16_t*>(out));
+  else if (head_dim == 256)
+    hipLaunchKernelGGL((lse_merge_kernel<256>), dim3(rows), dim3(256), 0, stream, part_o,
+                       part_ml, context_lens, ctx_clamp, plan.partition_blocks, plan.max_parts,
+                       num_q_heads, static_cast<uint16_t*>(out));
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t num_q_heads,
                        int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens) {

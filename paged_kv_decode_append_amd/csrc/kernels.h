@@ -45,6 +45,31 @@ hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_
                                const DecodePlan& plan, const DecodeAppend& app, void* out,
                                void* workspace, hipStream_t stream);
 
+// Log-sum-exp merge of the split-KV partitions written by a decode kernel
+// (partials [rows][max_parts] of (o / l) and (m, l)); rows with a single
+// partition were written by the decode kernel and are skipped.
+hipError_t launch_decode_merge(const float* part_o, const float* part_ml,
+                               const int32_t* context_lens, int32_t ctx_clamp,
+                               const DecodePlan& plan, int32_t num_decode_seqs,
+                               int32_t num_q_heads, int32_t head_dim, void* out,
+                               hipStream_t stream);
+
+// fp8 (OCP E4M3) cache (kv_fp8.hip): the quantizing append, and paged decode
+// over the codes with the same plan, partials and merge as the fp16 kernel.
+hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int32_t num_tokens,
+                                hipStream_t stream);
+
+hipError_t launch_paged_decode_fp8(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                                   int32_t head_dim, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                                   void* out, void* workspace, hipStream_t stream);
+
 // Balanced decode schedule (decode_sched.hip): made once per step on the
 // device from the context lengths, read by every layer's decode launch.
 struct DecodeSchedulePlan {

@@ -1,0 +1,571 @@
+// kv_fp8.hip -- the quantized (fp8, OCP E4M3) KV cache: the append that
+// quantizes each new K/V row, and paged decode attention reading the codes.
+//
+// Why: decode reads the whole cache every step and is bound by HBM, and the
+// raw KV of a window halves at 8 bits ("8 GiB at 8-bit ... before scales"
+// for a 262,144-token window -- a8q9.cn, "An advertised batch limit proves
+// nothing until sampled"; quantizing the cache is one of the remedies when
+// memory caps the batch -- deepconcepts.dev, "Continuous Batching Is Not a
+// Bigger Batch", "Checking it on a real system").
+//
+// Format (the pages fix none; the reading taken): codes are OCP E4M3 bytes in
+// the same [block][KV head][16][d] layout as the fp16 pools; every (token, KV
+// head) row carries one fp32 scale 2^e, the smallest power of two with
+// max|x| <= 448 x 2^e, so scaling is exact and the codes are x / 2^e rounded
+// to nearest (ties to even) by v_cvt_pk_fp8_f32.  The row value is code x 2^e.
+//
+// Decode works like the fp16 kernel (decode.hip): grid (sequence, KV head,
+// partition), 4 waves dealt the partition's blocks round-robin, the G query
+// heads of the group applied to each K/V byte once, base-2 online softmax
+// with a lazy maximum, masking by select, and the same partials and merge.
+// Per block and wave:
+//   K: D/16 lanes per token row, 16 codes (one 16-byte load) per lane; codes
+//     become fp16 pairs with v_cvt_scalef32_pk_f16_fp8 (exact: every E4M3
+//     value is an fp16 value), q.k is v_dot2_f32_f16 as in fp16, and the
+//     row's scale multiplies the score.
+//   V: at d = 128 lanes 0-31 take the even tokens of a block and lanes 32-63
+//     the odd ones, four columns each (a 4-byte load per token: 8 registers
+//     per block), and the two halves are added once at the end; at d = 256
+//     every lane owns 4 columns of all 16 tokens.  Two tokens' codes of one
+//     column are put side by side with v_perm_b32 and converted together, so
+//     P.V stays v_dot2 over token pairs.  The row scales 2^e_t enter the weights: each weight is scaled by
+//     2^(e_t - e_max) (e_max the block's largest, so weights stay within
+//     fp16), the block's P.V sum is formed apart and added times 2^e_max; the
+//     softmax denominator sums the unscaled weights.
+// Half the bytes per block let each wave keep four blocks in flight at
+// d = 128 (two at d = 256 for G <= 5), the same bytes in flight as the fp16
+// kernel.
+#include <algorithm>
+#include <climits>
+
+#include "device_util.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kBlockSize = 16;
+constexpr int kWaves = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.f;  // lazy max (base 2)
+
+// Smallest e with amax <= 448 x 2^e (0 for amax = 0).  amax is a finite fp16
+// value, a normal fp32 number: amax = 1.f x 2^k; 448 = 1.75 x 2^8, so
+// e = k - 8, plus 1 when the fraction f exceeds 0.75.
+__device__ __forceinline__ int row_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int k = (int)((b >> 23) & 0xFF) - 127;
+  return k - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+}
+
+// 2^e as fp32 for |e| <= 126.
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// ---------------------------------------------------------------- append ---
+
+// One wave per (token, KV head) row of K (grid.y = 0) or V (grid.y = 1),
+// four rows per work-group; lane l quantizes values EPL*l .. EPL*l + EPL-1.
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, int64_t rows) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int64_t t = r / num_kv_heads;
+  const int g = (int)(r - t * num_kv_heads);
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;  // padding: nothing to write
+  const int64_t b = slot / kBlockSize;
+  if (b >= num_blocks) return;  // beyond the pool (a broken contract): skipped
+  const int o = (int)(slot % kBlockSize);
+  const bool is_v = blockIdx.y == 1;
+  const uint16_t* src = (is_v ? v_new : k_new) + r * D + EPL * lane;
+  float x[EPL];
+  if constexpr (EPL == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu));
+    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x & 0xffffu));
+    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x >> 16));
+    x[2] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y & 0xffffu));
+    x[3] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y >> 16));
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int e = row_exponent(amax);
+  const float inv = exp2i(-e);  // exact scaling: |x * inv| <= 448
+  const int64_t row = ((b * num_kv_heads + g) * kBlockSize + o);
+  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D + EPL * lane;
+  if constexpr (EPL == 2) {
+    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(c & 0xffffu);
+  } else {
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, c, true);
+    *reinterpret_cast<uint32_t*>(dst) = (uint32_t)c;
+  }
+  if (lane == 0) (is_v ? v_scale : k_scale)[row] = exp2i(e);
+}
+
+// ---------------------------------------------------------------- decode ---
+
+// Two E4M3 codes (bytes 0-1 when hi is false, 2-3 when true) to an fp16 pair.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_h2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// V layout: at d = 128 a half-wave per token parity (HALF), 4 columns per
+// lane, 8 tokens; at d = 256 4 columns per lane, all 16 tokens.
+template <int D>
+struct V8Layout {
+  static constexpr bool HALF = D == 128;
+  static constexpr int TOK = HALF ? 8 : 16;  // tokens per lane
+  static constexpr int COLS = 4;             // columns per lane
+};
+
+template <int D>
+struct KV8Regs {
+  static constexpr int LPT = D / 16;    // lanes per K row
+  static constexpr int TPS = 64 / LPT;  // K rows per wave-wide load
+  static constexpr int SPB = 16 / TPS;  // K loads per block
+  uint4 k[SPB];                         // 16 codes of row tl + TPS*s
+  float ks[SPB];                        // that row's K scale
+  float vs[SPB];                        // and its V scale
+  uint32_t v[V8Layout<D>::TOK];         // 4 V codes of each of this lane's tokens
+};
+
+template <int D, int G>
+struct Wave8 {
+  float m[G];
+  float l[G];
+  float acc[G][V8Layout<D>::COLS];  // this lane's columns (d = 128: its token parity)
+};
+
+template <int D>
+__device__ __forceinline__ void load8(KV8Regs<D>& r, const uint8_t* __restrict__ kt,
+                                      const uint8_t* __restrict__ vt,
+                                      const float* __restrict__ kst,
+                                      const float* __restrict__ vst, int lane) {
+  constexpr int LPT = KV8Regs<D>::LPT, TPS = KV8Regs<D>::TPS, SPB = KV8Regs<D>::SPB;
+  const int tl = lane / LPT, c = lane % LPT;
+#pragma unroll
+  for (int s = 0; s < SPB; ++s) {
+    r.k[s] = *reinterpret_cast<const uint4*>(kt + (tl + TPS * s) * D + 16 * c);
+    r.ks[s] = kst[tl + TPS * s];
+    r.vs[s] = vst[tl + TPS * s];
+  }
+  if constexpr (V8Layout<D>::HALF) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)  // token 2j + half, columns 4 (lane % 32) ..
+      r.v[j] = *reinterpret_cast<const uint32_t*>(vt + (2 * j + (lane >> 5)) * D + 4 * (lane & 31));
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      r.v[t] = *reinterpret_cast<const uint32_t*>(vt + t * D + 4 * lane);
+  }
+}
+
+__device__ __forceinline__ float dot16_8(const uint32_t (&q)[8], const uint4& k) {
+  float s = 0.f;
+  s = dot2(q[0], fp8x2_to_h2<false>(k.x), s);
+  s = dot2(q[1], fp8x2_to_h2<true>(k.x), s);
+  s = dot2(q[2], fp8x2_to_h2<false>(k.y), s);
+  s = dot2(q[3], fp8x2_to_h2<true>(k.y), s);
+  s = dot2(q[4], fp8x2_to_h2<false>(k.z), s);
+  s = dot2(q[5], fp8x2_to_h2<true>(k.z), s);
+  s = dot2(q[6], fp8x2_to_h2<false>(k.w), s);
+  s = dot2(q[7], fp8x2_to_h2<true>(k.w), s);
+  return s;
+}
+
+// Scores, online softmax and the weights (to LDS) of one block; returns the
+// block's largest V scale (2^e_max, wave-uniform) for block_pv8.
+template <int D, int G>
+__device__ __forceinline__ float block_scores8(const KV8Regs<D>& r, const uint16_t* qs,
+                                               Wave8<D, G>& st, int tok0, int ctx,
+                                               float scale_log2, uint32_t* __restrict__ p_lds,
+                                               int lane) {
+  constexpr int LPT = KV8Regs<D>::LPT, TPS = KV8Regs<D>::TPS, SPB = KV8Regs<D>::SPB;
+  constexpr int GP = (G + 3) & ~3;
+  const int tl = lane / LPT, c = lane % LPT;
+  const float kNegInf = -__builtin_huge_valf();
+  asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
+  bool valid[SPB];
+#pragma unroll
+  for (int s = 0; s < SPB; ++s) valid[s] = tok0 + tl + TPS * s < ctx;
+
+  float x[SPB][G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint4 qa = *reinterpret_cast<const uint4*>(qs + h * D + 16 * c);
+    const uint4 qb = *reinterpret_cast<const uint4*>(qs + h * D + 16 * c + 8);
+    const uint32_t qh[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+    for (int s = 0; s < SPB; ++s) {
+      const float dot = group_sum<LPT>(dot16_8(qh, r.k[s]));
+      // select, not multiply: a stale row's scale or codes may be anything
+      x[s][h] = valid[s] ? dot * (r.ks[s] * scale_log2) : kNegInf;
+    }
+  }
+
+  bool grow = false;
+#pragma unroll
+  for (int s = 0; s < SPB; ++s)
+#pragma unroll
+    for (int h = 0; h < G; ++h) grow |= x[s][h] > st.m[h] + kRescaleSlack;
+  if (__any(grow)) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float bm = x[0][h];
+#pragma unroll
+      for (int s = 1; s < SPB; ++s) bm = fmaxf(bm, x[s][h]);
+#pragma unroll
+      for (int off = LPT; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+      const float mn = fmaxf(st.m[h], bm);
+      const float alpha = fast_exp2(st.m[h] - mn);
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < V8Layout<D>::COLS; ++e) st.acc[h][e] *= alpha;
+      st.m[h] = mn;
+    }
+  }
+
+  // the block's largest V scale over valid rows
+  float vsv[SPB];
+  float vmax = 0.f;
+#pragma unroll
+  for (int s = 0; s < SPB; ++s) {
+    vsv[s] = valid[s] ? r.vs[s] : 0.f;
+    vmax = fmaxf(vmax, vsv[s]);
+  }
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  const float inv_vmax = vmax > 0.f ? 1.f / vmax : 0.f;  // a power of two: exact
+
+  uint32_t pp[SPB / 2][G];
+#pragma unroll
+  for (int j = 0; j < SPB / 2; ++j) {
+    const float ra = vsv[2 * j] * inv_vmax, rb = vsv[2 * j + 1] * inv_vmax;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pa = fast_exp2(x[2 * j][h] - st.m[h]);
+      const float pb = fast_exp2(x[2 * j + 1][h] - st.m[h]);
+      st.l[h] += pa + pb;
+      pp[j][h] = pack_h2_rtz(pa * ra, pb * rb);
+    }
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int j = 0; j < SPB / 2; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) p_lds[(j * TPS + tl) * GP + h] = pp[j][h];
+  }
+  wave_fence();
+  return vmax;
+}
+
+template <int D, int G>
+__device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int tok0, int ctx,
+                                          const uint32_t* __restrict__ p_lds, float vmax,
+                                          int lane) {
+  constexpr int TPS = KV8Regs<D>::TPS;
+  constexpr int GP = (G + 3) & ~3;
+  constexpr bool HALF = V8Layout<D>::HALF;
+  constexpr int TOK = V8Layout<D>::TOK;
+  const int half = lane >> 5;
+  // token of this lane's v[j]
+  auto tok = [&](int j) { return HALF ? 2 * j + half : j; };
+  if (tok0 + 16 > ctx) {
+#pragma unroll
+    for (int j = 0; j < TOK; ++j)
+      if (tok0 + tok(j) >= ctx) r.v[j] = 0u;  // code 0 = +0: stale rows never leak
+  }
+  float tmp[G][4];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tmp[h][e] = 0.f;
+  // LDS pair pi holds tokens ta = pi % TPS + 2 TPS (pi / TPS) and ta + TPS.
+  // d = 128 (TPS = 8): pairs (pi, pi + 8); this half takes pi = 2m + half,
+  // tokens v[m] and v[m + 4].
+  constexpr int PAIRS = HALF ? 4 : 8;
+#pragma unroll
+  for (int m = 0; m < PAIRS; ++m) {
+    int pi, ja, jb;
+    if constexpr (HALF) {
+      pi = 2 * m + half;
+      ja = m;
+      jb = m + 4;
+    } else {
+      pi = m;
+      ja = m % TPS + 2 * TPS * (m / TPS);
+      jb = ja + TPS;
+    }
+    uint32_t pr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
+    // bytes {a0, b0, a1, b1} and {a2, b2, a3, b3}: token pairs per column
+    const uint32_t x01 = __builtin_amdgcn_perm(r.v[jb], r.v[ja], 0x05010400u);
+    const uint32_t x23 = __builtin_amdgcn_perm(r.v[jb], r.v[ja], 0x07030602u);
+    const uint32_t col[4] = {fp8x2_to_h2<false>(x01), fp8x2_to_h2<true>(x01),
+                             fp8x2_to_h2<false>(x23), fp8x2_to_h2<true>(x23)};
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmp[h][e] = dot2(pr[h], col[e], tmp[h][e]);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.acc[h][e] = __builtin_fmaf(tmp[h][e], vmax, st.acc[h][e]);
+  wave_fence();
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
+    const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
+    const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
+    const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
+    int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int LPT = D / 16, GP = (G + 3) & ~3;
+  // blocks in flight per wave: 16 KiB at d = 128 and at d = 256 up to G = 5
+  // (larger groups keep one block, to stay within 256 registers)
+  constexpr int NBUF = D == 128 ? 4 : (G <= 5 ? 2 : 1);
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_m[kWaves][G];
+  __shared__ float s_l[kWaves][G];
+  __shared__ uint32_t s_p[kWaves][8 * GP];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
+
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
+  const int num_q_heads = num_kv_heads * G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b0 = part * partition_blocks;
+  const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
+
+  uint32_t raw_bid = 0;
+  {
+    const int e = b0 + wave + kWaves * lane;
+    if (wave + kWaves * lane < partition_blocks && e < max_blocks_per_seq)
+      raw_bid = (uint32_t)bt_row[e];
+  }
+  const uint4* qsrc =
+      reinterpret_cast<const uint4*>(q + ((int64_t)i * num_q_heads + (int64_t)g * G) * D);
+  constexpr int QCH = G * D / 8;
+  uint4 qstage[(QCH + 255) / 256];
+#pragma unroll
+  for (int k = 0; k < (QCH + 255) / 256; ++k)
+    if (tid + 256 * k < QCH) qstage[k] = qsrc[tid + 256 * k];
+
+  const int ctx = min(context_lens[i], ctx_clamp);
+  const int nblk = (ctx + 15) >> 4;
+  if (ctx <= 0 || b0 >= nblk) return;  // uniform over the work-group
+  const int b1 = min(b0 + partition_blocks, nblk);
+  const int nparts = (nblk + partition_blocks - 1) / partition_blocks;
+
+  const int nbw = (b1 - b0 - wave + kWaves - 1) / kWaves;
+  const int my_bid =
+      lane < nbw ? (int)(raw_bid < (uint64_t)num_blocks ? raw_bid : (uint32_t)(num_blocks - 1))
+                 : 0;
+  const int64_t tile = (int64_t)16 * D;           // bytes of one block of one head
+  const int64_t head_off = (int64_t)g * tile;
+  const int64_t block_stride = (int64_t)num_kv_heads * tile;
+  auto load_block = [&](KV8Regs<D>& r, int k) {
+    const int64_t bid = __builtin_amdgcn_readlane(my_bid, k);
+    const int64_t o = bid * block_stride + head_off;
+    const int64_t so = (bid * num_kv_heads + g) * 16;
+    load8<D>(r, k_codes + o, v_codes + o, k_scale + so, v_scale + so, lane);
+  };
+
+  KV8Regs<D> buf[NBUF];
+#pragma unroll
+  for (int j = 0; j < NBUF; ++j)
+    if (j < nbw) load_block(buf[j], j);
+#pragma unroll
+  for (int k = 0; k < (QCH + 255) / 256; ++k)
+    if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
+  __syncthreads();
+
+  Wave8<D, G> st;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = -__builtin_huge_valf();
+    st.l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.acc[h][e] = 0.f;
+  }
+  auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
+  for (int k = 0; k < nbw; k += NBUF) {
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) {
+      if (k + j >= nbw) break;
+      const float vmax =
+          block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2, s_p[wave], lane);
+      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, lane);
+      if (k + j + NBUF < nbw) load_block(buf[j], k + j + NBUF);
+    }
+  }
+
+  // Lane groups' weight sums -> wave totals; the two token halves' columns
+  // (d = 128) added; then merge the 4 waves.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float lw = st.l[h];
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
+    if constexpr (V8Layout<D>::HALF) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.acc[h][e] += __shfl_xor(st.acc[h][e], 32);
+      if (lane < 32)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_acc[wave][h][4 * lane + e] = st.acc[h][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_acc[wave][h][4 * lane + e] = st.acc[h][e];
+    }
+    if (lane == 0) {
+      s_m[wave][h] = st.m[h];
+      s_l[wave][h] = lw;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 64 * kWaves) {
+    const int h = idx / D, e = idx - h * D;
+    float M = -__builtin_huge_valf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      if (s_l[w][h] > 0.f) {
+        const float wt = fast_exp2(s_m[w][h] - M);
+        L += wt * s_l[w][h];
+        O += wt * s_acc[w][h][e];
+      }
+    }
+    const int64_t row_head = (int64_t)i * num_q_heads + g * G + h;
+    if (nparts == 1) {
+      out[row_head * D + e] = __builtin_bit_cast(uint16_t, (f16)(O / L));
+    } else {
+      const int64_t pidx = row_head * max_parts + part;
+      part_o[pidx * D + e] = O / L;
+      if (e == 0) {
+        part_ml[pidx * 2] = M;
+        part_ml[pidx * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t launch_decode_fp8_dg(const void* q, const void* k_codes, const void* v_codes,
+                                const float* k_scale, const float* v_scale, int64_t num_blocks,
+                                int32_t num_kv_heads, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                                void* out, void* workspace, hipStream_t stream) {
+  const int32_t num_q_heads = num_kv_heads * G;
+  const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
+                                            (int64_t)plan.max_parts * plan.partition_blocks * 16);
+  const int32_t ctx_clamp = (int32_t)std::min<int64_t>(clamp64, INT32_MAX);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_ml =
+      part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  hipLaunchKernelGGL((paged_decode_fp8_kernel<D, G>),
+                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
+                     stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(v_codes),
+                     k_scale, v_scale, num_blocks, num_kv_heads, block_tables,
+                     max_blocks_per_seq, context_lens, ctx_clamp, plan.partition_blocks,
+                     plan.max_parts, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
+                     part_ml);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.max_parts <= 1) return err;
+  return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
+                             num_q_heads, D, out, stream);
+}
+
+template <int D>
+hipError_t launch_decode_fp8_d(int32_t group, const void* q, const void* kc, const void* vc,
+                               const float* ks, const float* vs, int64_t num_blocks,
+                               int32_t num_kv_heads, const int32_t* bt, int32_t maxblk,
+                               const int32_t* ctx, int32_t nseq, float scale,
+                               const DecodePlan& plan, void* out, void* ws, hipStream_t stream) {
+#define PKV_CASE(GG)                                                                        \
+  case GG:                                                                                 \
+    return launch_decode_fp8_dg<D, GG>(q, kc, vc, ks, vs, num_blocks, num_kv_heads, bt,    \
+                                       maxblk, ctx, nseq, scale, plan, out, ws, stream);
+  switch (group) {
+    PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
+    PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef PKV_CASE
+}
+
+}  // namespace
+
+hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                                int64_t num_blocks, int32_t num_kv_heads, int32_t head_dim,
+                                const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int32_t num_tokens,
+                                hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t rows = (int64_t)num_tokens * num_kv_heads;
+  const dim3 grid((uint32_t)((rows + 3) / 4), 2);
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  if (head_dim == 128)
+    hipLaunchKernelGGL(kv_append_fp8_kernel<128>, grid, dim3(256), 0, stream,
+                       static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
+                       v_scale, num_blocks, num_kv_heads, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slot_mapping, rows);
+  else if (head_dim == 256)
+    hipLaunchKernelGGL(kv_append_fp8_kernel<256>, grid, dim3(256), 0, stream,
+                       static_cast<uint8_t*>(k_codes), static_cast<uint8_t*>(v_codes), k_scale,
+                       v_scale, num_blocks, num_kv_heads, static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), slot_mapping, rows);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_decode_fp8(const void* q, const void* k_codes, const void* v_codes,
+                                   const float* k_scale, const float* v_scale,
+                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                                   int32_t head_dim, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+                                   void* out, void* workspace, hipStream_t stream) {
+  if (num_decode_seqs == 0) return hipSuccess;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (head_dim == 128)
+    return launch_decode_fp8_d<128>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
+                                    num_kv_heads, block_tables, max_blocks_per_seq,
+                                    context_lens, num_decode_seqs, scale, plan, out, workspace,
+                                    stream);
+  if (head_dim == 256)
+    return launch_decode_fp8_d<256>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
+                                    num_kv_heads, block_tables, max_blocks_per_seq,
+                                    context_lens, num_decode_seqs, scale, plan, out, workspace,
+                                    stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

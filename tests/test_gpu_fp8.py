@@ -1,0 +1,190 @@
+"""GPU parity of the fp8 (OCP E4M3) KV cache against the CPU oracle:
+the quantizing append bit for bit (codes and scales, on rows that together
+hold every finite fp16 value, so every rounding the hardware conversion
+makes is checked), and paged decode over fp8 pools within the attention
+tolerance of the fp16 path (the oracle attends the exactly dequantized
+cache, so the same rounding budget applies)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_append_amd as pkv
+import workloads
+from oracle import fp8 as ofp8
+from paged_kv_decode_append_amd.step import Step
+from parity import assert_close, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(name, errs):
+    print(f"[parity] {name}: max_abs={errs[0]:.2e} norm_rel={errs[1]:.2e}", flush=True)
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _all_finite_fp16_rows(d):
+    """Every finite fp16 value once, sorted by magnitude and cut into rows of
+    d (a row's values are close in size, so its codes span the format), plus
+    the same values shuffled into rows (a row's small values meet its large
+    scale)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    finite = bits[np.isfinite(vals)]
+    order = np.argsort(np.abs(finite.view(np.float16).astype(np.float64)), kind="stable")
+    sorted_bits = finite[order]
+    shuffled = np.random.default_rng(3).permutation(finite)
+    allrows = np.concatenate([sorted_bits, shuffled])
+    pad = (-len(allrows)) % d
+    allrows = np.concatenate([allrows, np.zeros(pad, np.uint16)])
+    return allrows.reshape(-1, d)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_append_quantizes_every_fp16_value_bit_exactly(d):
+    hkv = 2
+    rows = _all_finite_fp16_rows(d)                    # [R, d]
+    T = len(rows) // hkv
+    rows = rows[: T * hkv].reshape(T, hkv, d)
+    NB = (T + 15) // 16 + 3
+    rng = np.random.default_rng(d)
+    kc0 = rng.integers(0, 256, (NB, hkv, 16, d), dtype=np.uint8)
+    vc0 = rng.integers(0, 256, (NB, hkv, 16, d), dtype=np.uint8)
+    ks0 = rng.standard_normal((NB, hkv, 16)).astype(np.float32)
+    vs0 = rng.standard_normal((NB, hkv, 16)).astype(np.float32)
+    slots = rng.permutation(NB * 16)[:T].astype(np.int64)
+    slots[::97] = -1                                    # padding tokens are skipped
+    k_new = rows
+    v_new = rows[::-1].copy()
+    dev = {n: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+           for n, a in (("kc", kc0), ("vc", vc0), ("ks", ks0), ("vs", vs0))}
+    cache = pkv.KVCache(dev["kc"], dev["vc"], dev["ks"], dev["vs"])
+    kn = torch.from_numpy(k_new.view(np.float16)).cuda()
+    vn = torch.from_numpy(np.ascontiguousarray(v_new).view(np.float16)).cuda()
+    pkv.kv_append(cache, kn, vn, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = ofp8.kv_append(kc0, vc0, ks0, vs0, k_new, v_new, slots)
+    assert np.array_equal(_np(dev["kc"]), kc), "K codes"
+    assert np.array_equal(_np(dev["vc"]), vc), "V codes"
+    assert np.array_equal(_np(dev["ks"]).view(np.uint32), ks.view(np.uint32)), "K scales"
+    assert np.array_equal(_np(dev["vs"]).view(np.uint32), vs.view(np.uint32)), "V scales"
+
+
+def _fp8_cache(wl, layer=0, poison=True):
+    t = workloads.layer_tensors_fp8(wl, layer, device="cuda")
+    if poison:
+        # stale rows (outside every context) hold NaN codes and NaN scales
+        qsl = np.concatenate([[0], np.cumsum(wl.context_lens)]).astype(np.int32)
+        live = np.zeros(wl.num_blocks * 16, bool)
+        live[oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, 16)] = True
+        dead = torch.from_numpy(np.nonzero(~live)[0]).cuda()
+        for n in ("k_codes", "v_codes"):
+            t[n].transpose(1, 2)[dead // 16, dead % 16] = 0x7F
+        for n in ("k_scale", "v_scale"):
+            t[n].transpose(1, 2)[dead // 16, dead % 16] = float("nan")
+    return t
+
+
+def _run(wl, t, part=0, fused=False):
+    step = Step.from_workload(wl, kv_partition_tokens=part)
+    step.plan()
+    cache = pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+    out = torch.full_like(t["q"], float("nan"))
+    step.layer(cache, t["q"], t["k_new"], t["v_new"], out, fused=fused)
+    torch.cuda.synchronize()
+    return step, out
+
+
+def _ref(wl, t, q=None, seq_subset=None):
+    return oracle.paged_attention_fp8(host_bits(t["q"]) if q is None else q, _np(t["k_codes"]),
+                                      _np(t["v_codes"]), _np(t["k_scale"]), _np(t["v_scale"]),
+                                      wl.block_tables, wl.context_lens, None, wl.scale,
+                                      seq_subset=seq_subset)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 12, 2), (128, 8, 8), (128, 8, 1), (128, 24, 3),
+                                      (256, 16, 4), (256, 8, 8), (256, 12, 2), (256, 24, 3)])
+@pytest.mark.parametrize("part", [0, 64, 256])
+def test_decode_over_an_fp8_cache(d, hq, hkv, part):
+    ctx = [1, 2, 15, 16, 17, 31, 33, 64, 65, 300, 1025, 2500]
+    wl = workloads.custom("fp8", ctx, [1] * len(ctx), len(ctx), hq, hkv, d, seed=hq * d + part)
+    t = _fp8_cache(wl)
+    # attention only: the decode tokens' rows are already in the cache
+    step = Step.from_workload(wl, kv_partition_tokens=part)
+    cache = pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+    out = torch.full_like(t["q"], float("nan"))
+    pkv.paged_attention_step(cache, t["q"], out, step.block_tables, step.context_lens, None,
+                             wl.num_decode_seqs, wl.scale, step.max_context_len, 1,
+                             workspace=step.workspace, kv_partition_tokens=part)
+    torch.cuda.synchronize()
+    errs = assert_close(out.cpu().numpy(), _ref(wl, t), f"fp8 d={d} G={hq // hkv} part={part}")
+    _report(f"fp8 decode d={d} G={hq // hkv} part={part}", errs)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_single_position_returns_the_dequantized_value(d):
+    wl = workloads.custom("fp8_ctx1", [1, 1, 1], [1, 1, 1], 3, 2 * (d // 64), 2, d, seed=d)
+    t = _fp8_cache(wl, poison=False)
+    step = Step.from_workload(wl)
+    cache = pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+    out = torch.empty_like(t["q"])
+    pkv.paged_attention_step(cache, t["q"], out, step.block_tables, step.context_lens, None, 3,
+                             wl.scale, 1, 1, workspace=step.workspace)
+    torch.cuda.synchronize()
+    deq = ofp8.dequantize(_np(t["v_codes"]), _np(t["v_scale"]))   # exact, fits fp16
+    G = wl.num_q_heads // wl.num_kv_heads
+    got = out.cpu().numpy()
+    for i in range(3):
+        b = wl.block_tables[i, 0]
+        for h in range(wl.num_q_heads):
+            want = deq[b, h // G, 0].astype(np.float16)
+            assert np.array_equal(got[i, h].view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_step_appends_quantized_rows_then_attends(fused):
+    """The step's new tokens: quantized into their slots (bit-exact against
+    the oracle's append replay), then attended with the rest of the cache."""
+    ctx = [5, 16, 17, 100, 513, 2049]
+    wl = workloads.custom("fp8_step", ctx, [1] * len(ctx), len(ctx), 12, 2, 128, seed=29)
+    t = _fp8_cache(wl)
+    kc0, vc0, ks0, vs0 = (_np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale"))
+    step, out = _run(wl, t, fused=fused)
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, None, 16)
+    kc, vc, ks, vs = ofp8.kv_append(kc0, vc0, ks0, vs0, host_bits(t["k_new"]),
+                                    host_bits(t["v_new"]), slots)
+    assert np.array_equal(_np(t["k_codes"]), kc) and np.array_equal(_np(t["v_codes"]), vc)
+    assert np.array_equal(_np(t["k_scale"]).view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(_np(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, None, wl.scale)
+    _report(f"fp8 step fused={fused}", assert_close(out.cpu().numpy(), ref, "fp8 step"))
+
+
+def test_prefill_chunks_over_an_fp8_cache_are_refused():
+    wl = workloads.custom("fp8_chunk", [40, 20], [1, 8], 1, 12, 2, 128, seed=31)
+    t = _fp8_cache(wl, poison=False)
+    with pytest.raises(pkv.PkvError) as e:
+        _run(wl, t)
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["qwen_uniform", "qwen_ragged"])
+def test_full_size_fp8(name):
+    """One layer of the 28-layer workloads over an fp8 cache, sampled
+    sequences against the oracle."""
+    wl = workloads.WORKLOADS[name]()
+    t = _fp8_cache(wl, layer=3, poison=False)
+    _, out = _run(wl, t, fused=True)
+    kc, vc, ks, vs = ofp8.kv_append(*(_np(t[n]) for n in ("k_codes", "v_codes", "k_scale",
+                                                          "v_scale")),
+                                    host_bits(t["k_new"]), host_bits(t["v_new"]),
+                                    oracle.slot_mapping(wl.block_tables, wl.context_lens, None, 16))
+    subset = [0, 1, 17, 40, wl.num_seqs - 1]
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, None, wl.scale, seq_subset=subset)
+    errs = assert_close(out.cpu().numpy()[subset], ref[subset], name)
+    _report(f"{name} fp8 layer 3", errs)

@@ -220,6 +220,35 @@ def custom(name: str, ctx, new, num_decode_seqs: int, hq: int, hkv: int, d: int,
                   pool_blocks=pool_blocks)
 
 
+def layer_tensors_fp8(wl: Workload, layer: int, device="cpu"):
+    """An fp8 (E4M3) cache of one layer with N(0,1)-like values, drawn
+    directly as bytes: k_codes, v_codes uint8 [NB, Hkv, 16, d] with random
+    sign, exponent field 4..10 and mantissa (values 2^-3 .. ~15, no NaN
+    codes), k_scale, v_scale float32 [NB, Hkv, 16] random powers of two
+    2^-6 .. 2^-3; plus fp16 q, k_new, v_new as layer_tensors.  Seeded by
+    (seed, layer)."""
+    import torch
+
+    rng = np.random.default_rng([wl.seed, layer, 8])
+    shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+
+    def codes():
+        sign = rng.integers(0, 2, shape, dtype=np.uint8) << 7
+        expo = rng.integers(4, 11, shape, dtype=np.uint8) << 3
+        mant = rng.integers(0, 8, shape, dtype=np.uint8)
+        return torch.from_numpy(sign | expo | mant).to(device)
+
+    def scales():
+        e = rng.integers(-6, -2, shape[:3])
+        return torch.from_numpy(np.ldexp(1.0, e).astype(np.float32)).to(device)
+
+    t = layer_tensors(Workload(wl.name, wl.num_layers, wl.num_q_heads, wl.num_kv_heads,
+                               wl.head_dim, wl.context_lens, wl.new_tokens, wl.num_decode_seqs,
+                               1, wl.block_tables, wl.seed), layer, device)
+    return {"k_codes": codes(), "v_codes": codes(), "k_scale": scales(), "v_scale": scales(),
+            "q": t["q"], "k_new": t["k_new"], "v_new": t["v_new"]}
+
+
 def serving_requests(seed: int = 0, num_requests: int = 256, prompt_range=(256, 2480),
                      output_range=(50, 781), shared_prefix: int = 0, prefix_groups: int = 0):
     """A queue of requests for the per-pass scheduler: prompt lengths uniform
