@@ -191,13 +191,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   }
 
   WaveState<D, G> st;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = -__builtin_huge_valf();
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) st.acc[h][e] = 0.f;
-  }
+  wave_init(st);
 
   // Blocks k (in A) and k+1 (in B) per trip, buffer roles fixed so both stay
   // in registers.
@@ -240,19 +234,8 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     }
   }
 
-  // Lane groups' weight sums -> wave totals; then merge the 4 waves.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float lw = st.l[h];
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * lane + e] = st.acc[h][e];
-    if (lane == 0) {
-      s_m[wave][h] = st.m[h];
-      s_l[wave][h] = lw;
-    }
-  }
+  // Each wave's per-head totals to LDS; then merge the 4 waves.
+  wave_store<D, G>(st, s_acc[wave], s_m[wave], s_l[wave], lane);
   __syncthreads();
 
   for (int idx = tid; idx < G * D; idx += 64 * kWaves) {

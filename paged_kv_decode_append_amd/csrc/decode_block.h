@@ -3,19 +3,25 @@
 // 16-token K/V block of one KV head, its loads, the q.k scores with the
 // lazy-max online softmax, and the P.V accumulation.
 //
-// K layout: D/16 lanes share one token row, each lane holding 16 of its d
-//   values (two 16-byte chunks), so a K load instruction reads whole 128-byte
-//   runs of rows.  q.k is 8 packed fp16 dot products (v_dot2_f32_f16, fp32
-//   accumulate) per head with the query fragments read from LDS, then a DPP
-//   butterfly inside the lane group.
-// Online softmax, base 2: scores are scaled by scale*log2(e); the running max
-//   m is wave-uniform and only raised when a score exceeds it by more than
-//   kRescaleSlack (then the accumulators are rescaled), so weights
-//   p = 2^(s-m) stay in (0, 256] and the common case does no rescale.
+// Scores on the matrix cores: with grouped-query attention the G query heads
+// of a KV head read the same keys, so the scores of a block are a small dense
+// product S^T = K Q^T (16 tokens x d times d x G), one
+// v_mfma_f32_16x16x32_f16 per 32 values of d.  K is the A operand loaded
+// straight from the block (lane l holds 8 values of token row l % 16 at
+// column 32c + 8 (l / 16)); Q^T is the B operand read from LDS (column n =
+// query head n of the group; columns n >= G hold some head's query and their
+// scores are masked).  The result gives lane l the scores of head l % 16 for
+// tokens 4 (l / 16) .. +3.
+// Online softmax, base 2: scores are scaled by scale*log2(e); each lane keeps
+//   the running max m of its head and only raises it when a score passes it
+//   by more than kRescaleSlack (a wave vote; then the head's accumulators are
+//   rescaled), so weights p = 2^(s-m) stay in (0, 256] and the common case
+//   needs no cross-lane traffic at all.
 // V layout: every lane owns d/64 output elements of all 16 tokens, so the
 //   P.V accumulation needs no cross-lane reduction.  The weights travel from
-//   the K layout to all lanes through a small per-wave LDS buffer as fp16
-//   pairs of tokens, and P.V is again v_dot2_f32_f16 over those pairs.
+//   the score layout to all lanes through a small per-wave LDS buffer as
+//   fp16 pairs of consecutive tokens, and P.V is v_dot2_f32_f16 over those
+//   pairs (the VALU part, whose layout matches the cache's rows).
 // Masking is by select: positions >= ctx get score -inf and their V rows are
 //   zeroed before use, so stale or NaN-poisoned slots never leak.
 #pragma once
@@ -25,6 +31,9 @@
 namespace pkv {
 namespace decode_block {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kRescaleSlack = 8.f;  // lazy max: rescale only past m + 8 (base 2)
 
 template <int D> struct VFrag;
@@ -33,30 +42,53 @@ template <> struct VFrag<256> { typedef uint2 T; };
 
 template <int D>
 struct KVRegs {
-  static constexpr int LPT = D / 16;    // lanes sharing one K row
-  static constexpr int TPS = 64 / LPT;  // tokens covered by one wave-wide K load
-  static constexpr int SPB = 16 / TPS;  // K loads (steps) per 16-token block
-  uint4 k[SPB][2];
+  static constexpr int KC = D / 32;  // 32-wide chunks of d (MFMA K)
+  uint4 k[KC];                       // token row lane % 16, columns 32c + 8 (lane / 16) .. +7
   typename VFrag<D>::T v[16];
 };
 
 template <int D, int G>
 struct WaveState {
-  float m[G];           // running max of base-2 scores (wave-uniform)
-  float l[G];           // sum of weights over this lane group's tokens
+  float m;              // running max of this lane's head (lane % 16), base 2
+  float l;              // sum of its weights over this lane's tokens
   float acc[G][D / 64]; // sum of weight * v over this lane's output elements
 };
 
+template <int D, int G>
+__device__ __forceinline__ void wave_init(WaveState<D, G>& st) {
+  st.m = -__builtin_huge_valf();
+  st.l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) st.acc[h][e] = 0.f;
+}
+
+// The wave's partial (per head: max, weight sum, weighted V columns) into
+// per-wave LDS rows: s_acc_w[G][D], s_m_w[G], s_l_w[G].
+template <int D, int G>
+__device__ __forceinline__ void wave_store(const WaveState<D, G>& st, float (&s_acc_w)[G][D],
+                                           float (&s_m_w)[G], float (&s_l_w)[G], int lane) {
+  constexpr int EPL = D / 64;
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);  // the head's 16 tokens per block, over the 4 lane groups
+  const int row = lane & 15;
+  if (lane < 16 && row < G) {
+    s_m_w[row] = st.m;
+    s_l_w[row] = l;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) s_acc_w[h][EPL * lane + e] = st.acc[h][e];
+}
+
 template <int D>
 __device__ __forceinline__ void load_k(KVRegs<D>& r, const uint16_t* __restrict__ ktile, int lane) {
-  constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
-  const int tl = lane / LPT, c = lane % LPT;
 #pragma unroll
-  for (int s = 0; s < SPB; ++s)
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch)
-      r.k[s][ch] =
-          *reinterpret_cast<const uint4*>(ktile + (tl + TPS * s) * D + 8 * (c + LPT * ch));
+  for (int c = 0; c < KVRegs<D>::KC; ++c)
+    r.k[c] = *reinterpret_cast<const uint4*>(ktile + (lane & 15) * D + 32 * c + 8 * (lane >> 4));
 }
 
 template <int D>
@@ -64,19 +96,6 @@ __device__ __forceinline__ void load_v(KVRegs<D>& r, const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < 16; ++t)
     r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
-}
-
-__device__ __forceinline__ float dot16(const uint32_t (&q)[8], const uint4& a, const uint4& b) {
-  float s = 0.f;
-  s = dot2(q[0], a.x, s);
-  s = dot2(q[1], a.y, s);
-  s = dot2(q[2], a.z, s);
-  s = dot2(q[3], a.w, s);
-  s = dot2(q[4], b.x, s);
-  s = dot2(q[5], b.y, s);
-  s = dot2(q[6], b.z, s);
-  s = dot2(q[7], b.w, s);
-  return s;
 }
 
 // P.V over one token pair for one packed dword of V per token:
@@ -93,12 +112,11 @@ __device__ __forceinline__ void pv_dword(float (&acc)[G][2], const uint32_t (&pr
   }
 }
 
-// One 16-token block, first half: scores from the K registers, lazy-max
-// online softmax, weights to the wave's LDS buffer.  After it returns the K
-// registers are free (the next K load may target them).
+// One 16-token block, first half: scores on the matrix cores, lazy-max online
+// softmax, weights to the wave's LDS buffer (pair pi = tokens 2pi, 2pi + 1).
+// After it returns the K registers are free (the next K load may target them).
 // tok0 = logical position of the block's first token.
-// qs = the segment's G query rows in LDS ([G][D] fp16); each lane reads its
-// 16-value fragments per block instead of holding them in registers.
+// qs = the segment's G query rows in LDS ([G][D] fp16).
 // knew: when not null, the K row appended in this step for position ctx - 1
 // ([D] fp16 in LDS); it replaces that row of the block holding ctx - 1.
 template <int D, int G>
@@ -106,84 +124,63 @@ __device__ __forceinline__ void block_scores(KVRegs<D>& r, const uint16_t* qs,
                                              WaveState<D, G>& st, int tok0, int ctx,
                                              float scale_log2, uint32_t* __restrict__ p_lds,
                                              const uint16_t* knew, int lane) {
-  constexpr int LPT = KVRegs<D>::LPT, TPS = KVRegs<D>::TPS, SPB = KVRegs<D>::SPB;
+  constexpr int KC = KVRegs<D>::KC;
   constexpr int GP = (G + 3) & ~3;
-  const int tl = lane / LPT, c = lane % LPT;
-  const bool tail = tok0 + 16 > ctx;
+  static_assert(G <= 16, "one MFMA column per query head");
+  const int row = lane & 15, grp = lane >> 4;
   const float kNegInf = -__builtin_huge_valf();
   asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
-  if (knew != nullptr && tok0 + 16 >= ctx) {
-    const int row = ctx - 1 - tok0;
-    const uint4 n0 = *reinterpret_cast<const uint4*>(knew + 8 * c);
-    const uint4 n1 = *reinterpret_cast<const uint4*>(knew + 8 * (c + LPT));
+  if (knew != nullptr && tok0 + 16 >= ctx && row == ctx - 1 - tok0) {
 #pragma unroll
-    for (int s = 0; s < SPB; ++s)
-      if (tl + TPS * s == row) {
-        r.k[s][0] = n0;
-        r.k[s][1] = n1;
-      }
+    for (int c = 0; c < KC; ++c)
+      r.k[c] = *reinterpret_cast<const uint4*>(knew + 32 * c + 8 * grp);
   }
 
-  // Scores of this lane group's SPB tokens (tl + TPS*s) for every head.
-  float x[SPB][G];
+  // S^T = K Q^T: s[i] = score of head `row` with token 4 grp + i
+  const int hq = row < G ? row : 0;  // columns past G repeat head 0; masked below
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qa = *reinterpret_cast<const uint4*>(qs + h * D + 8 * c);
-    const uint4 qb = *reinterpret_cast<const uint4*>(qs + h * D + 8 * (c + LPT));
-    const uint32_t qh[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-    for (int s = 0; s < SPB; ++s)
-      x[s][h] = group_sum<LPT>(dot16(qh, r.k[s][0], r.k[s][1])) * scale_log2;
+  for (int c = 0; c < KC; ++c) {
+    const uint4 qv = *reinterpret_cast<const uint4*>(qs + hq * D + 32 * c + 8 * grp);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, r.k[c]),
+                                               __builtin_bit_cast(f16x8, qv), s, 0, 0, 0);
   }
-  if (tail) {
-#pragma unroll
-    for (int s = 0; s < SPB; ++s) {
-      const bool valid = tok0 + tl + TPS * s < ctx;
-#pragma unroll
-      for (int h = 0; h < G; ++h) x[s][h] = valid ? x[s][h] : kNegInf;
-    }
-  }
-
-  // Raise the running max only when a score passes it by the slack.
+  float x[4];
   bool grow = false;
 #pragma unroll
-  for (int s = 0; s < SPB; ++s)
-#pragma unroll
-    for (int h = 0; h < G; ++h) grow |= x[s][h] > st.m[h] + kRescaleSlack;
+  for (int i = 0; i < 4; ++i) {
+    const bool ok = row < G && tok0 + 4 * grp + i < ctx;
+    x[i] = ok ? s[i] * scale_log2 : kNegInf;
+    grow |= x[i] > st.m + kRescaleSlack;
+  }
   if (__any(grow)) {
+    // the head's block maximum over its 16 tokens (4 lane groups)
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(st.m, bm);
+    // a lane of no head (row >= G) stays at -inf with weight 0
+    const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+    st.m = mn;
+    // head h's factor lives in lane h
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float bm = x[0][h];
+      const float ah = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
 #pragma unroll
-      for (int s = 1; s < SPB; ++s) bm = fmaxf(bm, x[s][h]);
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-      const float mn = fmaxf(st.m[h], bm);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      st.l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < D / 64; ++e) st.acc[h][e] *= alpha;
-      st.m[h] = mn;
+      for (int e = 0; e < D / 64; ++e) st.acc[h][e] *= ah;
     }
   }
-
-  // Weights as fp16 pairs of tokens (tl + 2j*TPS, tl + (2j+1)*TPS); l sums
-  // exactly the rounded weights that P.V uses.
-  uint32_t pp[SPB / 2][G];
-#pragma unroll
-  for (int j = 0; j < SPB / 2; ++j)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      pp[j][h] = pack_h2_rtz(fast_exp2(x[2 * j][h] - st.m[h]),
-                             fast_exp2(x[2 * j + 1][h] - st.m[h]));
-      st.l[h] = dot2(pp[j][h], kOnesH2, st.l[h]);
-    }
-  // Pair index pi = j*TPS + tl; one writer lane per group.
-  if (c == 0) {
-#pragma unroll
-    for (int j = 0; j < SPB / 2; ++j)
-#pragma unroll
-      for (int h = 0; h < G; ++h) p_lds[(j * TPS + tl) * GP + h] = pp[j][h];
+  const float neg_m = st.m == kNegInf ? 0.f : -st.m;
+  const uint32_t pp0 = pack_h2_rtz(fast_exp2(x[0] + neg_m), fast_exp2(x[1] + neg_m));
+  const uint32_t pp1 = pack_h2_rtz(fast_exp2(x[2] + neg_m), fast_exp2(x[3] + neg_m));
+  // l sums exactly the rounded weights that P.V uses
+  st.l = dot2(pp0, kOnesH2, st.l);
+  st.l = dot2(pp1, kOnesH2, st.l);
+  if (row < G) {
+    p_lds[(2 * grp) * GP + row] = pp0;
+    p_lds[(2 * grp + 1) * GP + row] = pp1;
   }
   wave_fence();
 }
@@ -195,7 +192,6 @@ template <int D, int G>
 __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int tok0, int ctx,
                                          const uint32_t* __restrict__ p_lds,
                                          const uint16_t* vnew, int lane) {
-  constexpr int TPS = KVRegs<D>::TPS;
   constexpr int GP = (G + 3) & ~3;
   if (vnew != nullptr && tok0 + 16 >= ctx) {
     // one bit per token row, tested with constant t: keeps r.v in registers
@@ -212,10 +208,10 @@ __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int 
       if (tok0 + t >= ctx) r.v[t] = typename VFrag<D>::T{};
   }
 
-  // P.V: pair pi holds tokens ta = pi%TPS + 2*TPS*(pi/TPS) and tb = ta + TPS.
+  // P.V: pair pi holds tokens 2pi and 2pi + 1.
 #pragma unroll
   for (int pi = 0; pi < 8; ++pi) {
-    const int ta = pi % TPS + 2 * TPS * (pi / TPS), tb = ta + TPS;
+    const int ta = 2 * pi, tb = ta + 1;
     uint32_t pr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];

@@ -492,13 +492,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
       rnext = fetch_new(s_seg[s + 1]);
     }
 
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      st.m[h] = -__builtin_huge_valf();
-      st.l[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[h][e] = 0.f;
-    }
+    wave_init(st);
     const int nbw = nbw_of(sg);
     auto tok_of = [&](int kk) { return (sg.jb + wave + kWaves * kk) * 16; };
     for (int k = 0; k < nbw; k += 2) {
@@ -552,18 +546,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     }
 
     // merge the 4 waves of this segment
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float lw = st.l[h];
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][h][EPL * lane + e] = st.acc[h][e];
-      if (lane == 0) {
-        s_m[wave][h] = st.m[h];
-        s_l[wave][h] = lw;
-      }
-    }
+    wave_store<D, G>(st, s_acc[wave], s_m[wave], s_l[wave], lane);
     if (s + 1 < nseg) {
       stage_q(qnext, buf ^ 1);
       stage_new(rnext, buf ^ 1);

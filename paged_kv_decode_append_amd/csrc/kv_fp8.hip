@@ -287,11 +287,11 @@ __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int to
   const int half = lane >> 5;
   // token of this lane's v[j]
   auto tok = [&](int j) { return HALF ? 2 * j + half : j; };
-  if (tok0 + 16 > ctx) {
+  // code 0 = +0 for rows past the context: stale rows never leak (a select on
+  // every block, no branch: a branch around the buffer's registers would make
+  // the compiler copy them and wait for every load in flight)
 #pragma unroll
-    for (int j = 0; j < TOK; ++j)
-      if (tok0 + tok(j) >= ctx) r.v[j] = 0u;  // code 0 = +0: stale rows never leak
-  }
+  for (int j = 0; j < TOK; ++j) r.v[j] = tok0 + tok(j) < ctx ? r.v[j] : 0u;
   float tmp[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -386,8 +386,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   const int64_t tile = (int64_t)16 * D;           // bytes of one block of one head
   const int64_t head_off = (int64_t)g * tile;
   const int64_t block_stride = (int64_t)num_kv_heads * tile;
+  // Loads are issued unconditionally (a block index past the wave's last one
+  // re-reads that block, an L2 hit, and is never used): a load under a branch
+  // makes the compiler copy the buffer at the join and wait for all loads.
+  const int last = max(nbw - 1, 0);
   auto load_block = [&](KV8Regs<D>& r, int k) {
-    const int64_t bid = __builtin_amdgcn_readlane(my_bid, k);
+    const int64_t bid = __builtin_amdgcn_readlane(my_bid, min(k, last));
     const int64_t o = bid * block_stride + head_off;
     const int64_t so = (bid * num_kv_heads + g) * 16;
     load8<D>(r, k_codes + o, v_codes + o, k_scale + so, v_scale + so, lane);
@@ -395,8 +399,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
 
   KV8Regs<D> buf[NBUF];
 #pragma unroll
-  for (int j = 0; j < NBUF; ++j)
-    if (j < nbw) load_block(buf[j], j);
+  for (int j = 0; j < NBUF; ++j) load_block(buf[j], j);
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
       const float vmax =
           block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2, s_p[wave], lane);
       block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, lane);
-      if (k + j + NBUF < nbw) load_block(buf[j], k + j + NBUF);
+      load_block(buf[j], k + j + NBUF);
     }
   }
 
