@@ -19,19 +19,22 @@
 // heads of the group applied to each K/V byte once, base-2 online softmax
 // with a lazy maximum, masking by select, and the same partials and merge.
 // Per block and wave:
-//   K: D/16 lanes per token row, 16 codes (one 16-byte load) per lane; codes
-//     become fp16 pairs with v_cvt_scalef32_pk_f16_fp8 (exact: every E4M3
-//     value is an fp16 value), q.k is v_dot2_f32_f16 as in fp16, and the
-//     row's scale multiplies the score.
-//   V: at d = 128 lanes 0-31 take the even tokens of a block and lanes 32-63
-//     the odd ones, four columns each (a 4-byte load per token: 8 registers
-//     per block), and the two halves are added once at the end; at d = 256
-//     every lane owns 4 columns of all 16 tokens.  Two tokens' codes of one
-//     column are put side by side with v_perm_b32 and converted together, so
-//     P.V stays v_dot2 over token pairs.  The row scales 2^e_t enter the weights: each weight is scaled by
-//     2^(e_t - e_max) (e_max the block's largest, so weights stay within
-//     fp16), the block's P.V sum is formed apart and added times 2^e_max; the
-//     softmax denominator sums the unscaled weights.
+//   K: the scores are S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_f16,
+//     the G query heads as columns): lane l loads 16 codes of token row
+//     l % 16 and turns them into the A fragments of two 32-wide chunks with
+//     v_cvt_scalef32_pk_f16_fp8 (exact: every E4M3 value is an fp16 value);
+//     the query fragments are read from LDS in the same column order.  Each
+//     lane ends with the scores of head l % 16 for 4 tokens, times the rows'
+//     K scales.
+//   V: at d = 128 lanes 0-31 take tokens 0-7 of a block and lanes 32-63
+//     tokens 8-15, four columns each (a 4-byte load per token), and the two
+//     halves are added once at the end; at d = 256 every lane owns 4 columns
+//     of all 16 tokens.  Two consecutive tokens' codes of one column are put
+//     side by side with v_perm_b32 and converted together, so P.V is v_dot2
+//     over token pairs.  The row scales 2^e_t enter the weights: each weight
+//     is scaled by 2^(e_t - e_max) (e_max the block's largest, so weights stay
+//     within fp16), the block's P.V sum is formed apart and added times
+//     2^e_max; the softmax denominator sums the unscaled weights.
 // Half the bytes per block let each wave keep four blocks in flight at
 // d = 128 (two at d = 256 for G <= 5), the same bytes in flight as the fp16
 // kernel.
@@ -126,31 +129,35 @@ __device__ __forceinline__ uint32_t fp8x2_to_h2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
-// V layout: at d = 128 a half-wave per token parity (HALF), 4 columns per
-// lane, 8 tokens; at d = 256 4 columns per lane, all 16 tokens.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// V layout: at d = 128 lanes 0-31 hold tokens 0-7 and lanes 32-63 tokens
+// 8-15 of a block (HALF), 4 columns per lane; at d = 256 4 columns per lane
+// of all 16 tokens.
 template <int D>
 struct V8Layout {
   static constexpr bool HALF = D == 128;
   static constexpr int TOK = HALF ? 8 : 16;  // tokens per lane
-  static constexpr int COLS = 4;             // columns per lane
 };
 
+// K in the matrix cores' A layout: lane l holds 16 codes of token row l % 16
+// at columns 64 c2 + 16 (l / 16) .. +15, the fragments of chunks 2 c2 and
+// 2 c2 + 1 (the query fragments are read with the same column order).
 template <int D>
 struct KV8Regs {
-  static constexpr int LPT = D / 16;    // lanes per K row
-  static constexpr int TPS = 64 / LPT;  // K rows per wave-wide load
-  static constexpr int SPB = 16 / TPS;  // K loads per block
-  uint4 k[SPB];                         // 16 codes of row tl + TPS*s
-  float ks[SPB];                        // that row's K scale
-  float vs[SPB];                        // and its V scale
-  uint32_t v[V8Layout<D>::TOK];         // 4 V codes of each of this lane's tokens
+  static constexpr int K16 = D / 64;  // 16-code loads per lane
+  uint4 k[K16];
+  float4 ks;                          // K scales of tokens 4 (l / 16) .. +3
+  float4 vs;                          // their V scales
+  uint32_t v[V8Layout<D>::TOK];       // 4 V codes of each of this lane's tokens
 };
 
 template <int D, int G>
 struct Wave8 {
-  float m[G];
-  float l[G];
-  float acc[G][V8Layout<D>::COLS];  // this lane's columns (d = 128: its token parity)
+  float m;         // running max of this lane's head (lane % 16), base 2
+  float l;         // sum of its weights over this lane's tokens
+  float acc[G][4]; // this lane's 4 columns (d = 128: over its 8 tokens)
 };
 
 template <int D>
@@ -158,18 +165,16 @@ __device__ __forceinline__ void load8(KV8Regs<D>& r, const uint8_t* __restrict__
                                       const uint8_t* __restrict__ vt,
                                       const float* __restrict__ kst,
                                       const float* __restrict__ vst, int lane) {
-  constexpr int LPT = KV8Regs<D>::LPT, TPS = KV8Regs<D>::TPS, SPB = KV8Regs<D>::SPB;
-  const int tl = lane / LPT, c = lane % LPT;
+  const int row = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int s = 0; s < SPB; ++s) {
-    r.k[s] = *reinterpret_cast<const uint4*>(kt + (tl + TPS * s) * D + 16 * c);
-    r.ks[s] = kst[tl + TPS * s];
-    r.vs[s] = vst[tl + TPS * s];
-  }
+  for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2)
+    r.k[c2] = *reinterpret_cast<const uint4*>(kt + row * D + 64 * c2 + 16 * grp);
+  r.ks = *reinterpret_cast<const float4*>(kst + 4 * grp);
+  r.vs = *reinterpret_cast<const float4*>(vst + 4 * grp);
   if constexpr (V8Layout<D>::HALF) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)  // token 2j + half, columns 4 (lane % 32) ..
-      r.v[j] = *reinterpret_cast<const uint32_t*>(vt + (2 * j + (lane >> 5)) * D + 4 * (lane & 31));
+    for (int j = 0; j < 8; ++j)  // token 8 (lane / 32) + j, columns 4 (lane % 32) ..
+      r.v[j] = *reinterpret_cast<const uint32_t*>(vt + (8 * (lane >> 5) + j) * D + 4 * (lane & 31));
   } else {
 #pragma unroll
     for (int t = 0; t < 16; ++t)
@@ -177,100 +182,90 @@ __device__ __forceinline__ void load8(KV8Regs<D>& r, const uint8_t* __restrict__
   }
 }
 
-__device__ __forceinline__ float dot16_8(const uint32_t (&q)[8], const uint4& k) {
-  float s = 0.f;
-  s = dot2(q[0], fp8x2_to_h2<false>(k.x), s);
-  s = dot2(q[1], fp8x2_to_h2<true>(k.x), s);
-  s = dot2(q[2], fp8x2_to_h2<false>(k.y), s);
-  s = dot2(q[3], fp8x2_to_h2<true>(k.y), s);
-  s = dot2(q[4], fp8x2_to_h2<false>(k.z), s);
-  s = dot2(q[5], fp8x2_to_h2<true>(k.z), s);
-  s = dot2(q[6], fp8x2_to_h2<false>(k.w), s);
-  s = dot2(q[7], fp8x2_to_h2<true>(k.w), s);
-  return s;
+template <int D, int G>
+__device__ __forceinline__ void wave8_init(Wave8<D, G>& st) {
+  st.m = -__builtin_huge_valf();
+  st.l = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.acc[h][e] = 0.f;
 }
 
-// Scores, online softmax and the weights (to LDS) of one block; returns the
-// block's largest V scale (2^e_max, wave-uniform) for block_pv8.
+// Scores on the matrix cores (codes converted to fp16 pairs, exact), the K
+// row scales, lazy-max online softmax, weights (times the V row scales over
+// the block's largest) to LDS as pairs of consecutive tokens; returns the
+// block's largest V scale (wave-uniform) for block_pv8.
 template <int D, int G>
 __device__ __forceinline__ float block_scores8(const KV8Regs<D>& r, const uint16_t* qs,
                                                Wave8<D, G>& st, int tok0, int ctx,
                                                float scale_log2, uint32_t* __restrict__ p_lds,
                                                int lane) {
-  constexpr int LPT = KV8Regs<D>::LPT, TPS = KV8Regs<D>::TPS, SPB = KV8Regs<D>::SPB;
   constexpr int GP = (G + 3) & ~3;
-  const int tl = lane / LPT, c = lane % LPT;
+  static_assert(G <= 16, "one MFMA column per query head");
+  const int row = lane & 15, grp = lane >> 4;
   const float kNegInf = -__builtin_huge_valf();
   asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
-  bool valid[SPB];
+  const int hq = row < G ? row : 0;  // columns past G repeat head 0; masked below
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < SPB; ++s) valid[s] = tok0 + tl + TPS * s < ctx;
-
-  float x[SPB][G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 qa = *reinterpret_cast<const uint4*>(qs + h * D + 16 * c);
-    const uint4 qb = *reinterpret_cast<const uint4*>(qs + h * D + 16 * c + 8);
-    const uint32_t qh[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-    for (int s = 0; s < SPB; ++s) {
-      const float dot = group_sum<LPT>(dot16_8(qh, r.k[s]));
-      // select, not multiply: a stale row's scale or codes may be anything
-      x[s][h] = valid[s] ? dot * (r.ks[s] * scale_log2) : kNegInf;
-    }
+  for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2) {
+    const uint4 w = r.k[c2];
+    const uint4 a0 = {fp8x2_to_h2<false>(w.x), fp8x2_to_h2<true>(w.x),
+                      fp8x2_to_h2<false>(w.y), fp8x2_to_h2<true>(w.y)};
+    const uint4 a1 = {fp8x2_to_h2<false>(w.z), fp8x2_to_h2<true>(w.z),
+                      fp8x2_to_h2<false>(w.w), fp8x2_to_h2<true>(w.w)};
+    const uint16_t* qp = qs + hq * D + 64 * c2 + 16 * grp;
+    const uint4 q0 = *reinterpret_cast<const uint4*>(qp);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(qp + 8);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a0),
+                                               __builtin_bit_cast(f16x8, q0), s, 0, 0, 0);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a1),
+                                               __builtin_bit_cast(f16x8, q1), s, 0, 0, 0);
   }
-
+  const float ks[4] = {r.ks.x, r.ks.y, r.ks.z, r.ks.w};
+  const float vs[4] = {r.vs.x, r.vs.y, r.vs.z, r.vs.w};
+  float x[4], vsv[4];
   bool grow = false;
-#pragma unroll
-  for (int s = 0; s < SPB; ++s)
-#pragma unroll
-    for (int h = 0; h < G; ++h) grow |= x[s][h] > st.m[h] + kRescaleSlack;
-  if (__any(grow)) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = x[0][h];
-#pragma unroll
-      for (int s = 1; s < SPB; ++s) bm = fmaxf(bm, x[s][h]);
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
-      const float mn = fmaxf(st.m[h], bm);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      st.l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < V8Layout<D>::COLS; ++e) st.acc[h][e] *= alpha;
-      st.m[h] = mn;
-    }
-  }
-
-  // the block's largest V scale over valid rows
-  float vsv[SPB];
   float vmax = 0.f;
 #pragma unroll
-  for (int s = 0; s < SPB; ++s) {
-    vsv[s] = valid[s] ? r.vs[s] : 0.f;
-    vmax = fmaxf(vmax, vsv[s]);
+  for (int i = 0; i < 4; ++i) {
+    const bool valid = tok0 + 4 * grp + i < ctx;
+    // select, not multiply: a stale row's scale or codes may be anything
+    x[i] = row < G && valid ? s[i] * (ks[i] * scale_log2) : kNegInf;
+    grow |= x[i] > st.m + kRescaleSlack;
+    vsv[i] = valid ? vs[i] : 0.f;
+    vmax = fmaxf(vmax, vsv[i]);
   }
-#pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-  const float inv_vmax = vmax > 0.f ? 1.f / vmax : 0.f;  // a power of two: exact
-
-  uint32_t pp[SPB / 2][G];
-#pragma unroll
-  for (int j = 0; j < SPB / 2; ++j) {
-    const float ra = vsv[2 * j] * inv_vmax, rb = vsv[2 * j + 1] * inv_vmax;
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+  vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+  if (__any(grow)) {
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(st.m, bm);
+    const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
+    st.l *= alpha;
+    st.m = mn;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float pa = fast_exp2(x[2 * j][h] - st.m[h]);
-      const float pb = fast_exp2(x[2 * j + 1][h] - st.m[h]);
-      st.l[h] += pa + pb;
-      pp[j][h] = pack_h2_rtz(pa * ra, pb * rb);
+      const float ah = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.acc[h][e] *= ah;
     }
   }
-  if (c == 0) {
+  const float inv_vmax = vmax > 0.f ? 1.f / vmax : 0.f;  // a power of two: exact
+  const float neg_m = st.m == kNegInf ? 0.f : -st.m;
+  float p[4];
 #pragma unroll
-    for (int j = 0; j < SPB / 2; ++j)
-#pragma unroll
-      for (int h = 0; h < G; ++h) p_lds[(j * TPS + tl) * GP + h] = pp[j][h];
+  for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] + neg_m);
+  st.l += (p[0] + p[1]) + (p[2] + p[3]);
+  const uint32_t pp0 = pack_h2_rtz(p[0] * (vsv[0] * inv_vmax), p[1] * (vsv[1] * inv_vmax));
+  const uint32_t pp1 = pack_h2_rtz(p[2] * (vsv[2] * inv_vmax), p[3] * (vsv[3] * inv_vmax));
+  if (row < G) {
+    p_lds[(2 * grp) * GP + row] = pp0;
+    p_lds[(2 * grp + 1) * GP + row] = pp1;
   }
   wave_fence();
   return vmax;
@@ -280,45 +275,31 @@ template <int D, int G>
 __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int tok0, int ctx,
                                           const uint32_t* __restrict__ p_lds, float vmax,
                                           int lane) {
-  constexpr int TPS = KV8Regs<D>::TPS;
   constexpr int GP = (G + 3) & ~3;
   constexpr bool HALF = V8Layout<D>::HALF;
   constexpr int TOK = V8Layout<D>::TOK;
-  const int half = lane >> 5;
-  // token of this lane's v[j]
-  auto tok = [&](int j) { return HALF ? 2 * j + half : j; };
+  const int base = HALF ? 8 * (lane >> 5) : 0;  // first token of this lane's v[]
   // code 0 = +0 for rows past the context: stale rows never leak (a select on
   // every block, no branch: a branch around the buffer's registers would make
   // the compiler copy them and wait for every load in flight)
 #pragma unroll
-  for (int j = 0; j < TOK; ++j) r.v[j] = tok0 + tok(j) < ctx ? r.v[j] : 0u;
+  for (int j = 0; j < TOK; ++j) r.v[j] = tok0 + base + j < ctx ? r.v[j] : 0u;
   float tmp[G][4];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 4; ++e) tmp[h][e] = 0.f;
-  // LDS pair pi holds tokens ta = pi % TPS + 2 TPS (pi / TPS) and ta + TPS.
-  // d = 128 (TPS = 8): pairs (pi, pi + 8); this half takes pi = 2m + half,
-  // tokens v[m] and v[m + 4].
-  constexpr int PAIRS = HALF ? 4 : 8;
+  // LDS pair pi holds tokens 2pi and 2pi + 1: this lane's pairs are its
+  // v[2m], v[2m + 1] at pi = base / 2 + m.
 #pragma unroll
-  for (int m = 0; m < PAIRS; ++m) {
-    int pi, ja, jb;
-    if constexpr (HALF) {
-      pi = 2 * m + half;
-      ja = m;
-      jb = m + 4;
-    } else {
-      pi = m;
-      ja = m % TPS + 2 * TPS * (m / TPS);
-      jb = ja + TPS;
-    }
+  for (int m = 0; m < TOK / 2; ++m) {
+    const int pi = base / 2 + m;
     uint32_t pr[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
     // bytes {a0, b0, a1, b1} and {a2, b2, a3, b3}: token pairs per column
-    const uint32_t x01 = __builtin_amdgcn_perm(r.v[jb], r.v[ja], 0x05010400u);
-    const uint32_t x23 = __builtin_amdgcn_perm(r.v[jb], r.v[ja], 0x07030602u);
+    const uint32_t x01 = __builtin_amdgcn_perm(r.v[2 * m + 1], r.v[2 * m], 0x05010400u);
+    const uint32_t x23 = __builtin_amdgcn_perm(r.v[2 * m + 1], r.v[2 * m], 0x07030602u);
     const uint32_t col[4] = {fp8x2_to_h2<false>(x01), fp8x2_to_h2<true>(x01),
                              fp8x2_to_h2<false>(x23), fp8x2_to_h2<true>(x23)};
 #pragma unroll
@@ -342,7 +323,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  constexpr int LPT = D / 16, GP = (G + 3) & ~3;
+  constexpr int GP = (G + 3) & ~3;
   // blocks in flight per wave: 16 KiB at d = 128 and at d = 256 up to G = 5
   // (larger groups keep one block, to stay within 256 registers)
   constexpr int NBUF = D == 128 ? 4 : (G <= 5 ? 2 : 1);
@@ -406,13 +387,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   __syncthreads();
 
   Wave8<D, G> st;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = -__builtin_huge_valf();
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st.acc[h][e] = 0.f;
-  }
+  wave8_init(st);
   auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
   for (int k = 0; k < nbw; k += NBUF) {
 #pragma unroll
@@ -425,13 +400,17 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     }
   }
 
-  // Lane groups' weight sums -> wave totals; the two token halves' columns
-  // (d = 128) added; then merge the 4 waves.
+  // The wave's per-head totals to LDS (the two token halves' columns added
+  // at d = 128); then merge the 4 waves.
+  float lw = st.l;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+  if (lane < 16 && lane < G) {
+    s_m[wave][lane] = st.m;
+    s_l[wave][lane] = lw;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float lw = st.l[h];
-#pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) lw += __shfl_xor(lw, off);
     if constexpr (V8Layout<D>::HALF) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.acc[h][e] += __shfl_xor(st.acc[h][e], 32);
@@ -441,10 +420,6 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) s_acc[wave][h][4 * lane + e] = st.acc[h][e];
-    }
-    if (lane == 0) {
-      s_m[wave][h] = st.m[h];
-      s_l[wave][h] = lw;
     }
   }
   __syncthreads();
