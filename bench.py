@@ -70,6 +70,9 @@ def parse():
                     help="capture the whole step (all layers) once as a HIP graph and time "
                          "its replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-dtype", choices=["fp16", "fp8"], default="fp16",
+                    help="cache element type: fp16 (the workloads' own), or fp8 E4M3 codes "
+                         "with fp32 row scales (decode steps only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (5 times), the "
                          "reference for scaling HBM traffic counters, and exit")
@@ -77,18 +80,26 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes_per_attention_launch(wl, fused: bool) -> int:
+def kv_row_bytes(wl, kv_dtype: str) -> int:
+    """Cache bytes of one (token, KV head) row: d fp16 values, or d fp8 codes
+    and one fp32 scale."""
+    return wl.head_dim * 2 if kv_dtype == "fp16" else wl.head_dim + 4
+
+
+def algorithmic_bytes_per_attention_launch(wl, fused: bool, kv_dtype: str = "fp16") -> int:
     """For the sequences whose attention streams the cache (decodes, and
     multi-token decodes whose G x n rows fit one tile): KV of every context +
     Q and O rows + block ids, one layer; when the call also appends their new
-    tokens, + those K/V rows read and written and their slots."""
+    tokens, + those fp16 K/V rows read, their cache rows written, and their
+    slots."""
     m = wl.short_chunk()
     ctx = wl.context_lens[m].astype(np.int64)
     T = int(wl.new_tokens[m].sum())
-    kv = int(ctx.sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    row = kv_row_bytes(wl, kv_dtype)
+    kv = int(ctx.sum()) * wl.num_kv_heads * row * 2
     qo = 2 * T * wl.num_q_heads * wl.head_dim * 2
     ids = int((-(-ctx // wl.block_size)).sum()) * 4
-    app = (2 * 2 * T * wl.num_kv_heads * wl.head_dim * 2 + 8 * T) if fused else 0
+    app = (2 * T * wl.num_kv_heads * (wl.head_dim * 2 + row) + 8 * T) if fused else 0
     return kv + qo + ids + app
 
 
@@ -175,20 +186,31 @@ def prefill_roofline(wl, caches, layers, outs):
             "kernel": "chunked-prefill attention on MFMA (+ its split-KV merge)"}
 
 
-def cpu_baseline(wl, layer_tensors_dev, budget_s: float):
+def cpu_baseline(wl, layer_tensors_dev, budget_s: float, kv_dtype: str = "fp16"):
     """Time the oracle (append replay + attention, fp64) on whole layers of
     the step until the budget is spent; scale to decode tokens/s of a step."""
     import torch
     import oracle
+    from oracle import fp8 as ofp8
 
     qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None
     slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, wl.block_size)
     spent, layers = 0.0, 0
     for t in layer_tensors_dev:
-        host = {k: v.detach().cpu().view(torch.int16).numpy().view(np.uint16) for k, v in t.items()}
+        host = {k: (v.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+                    if v.dtype == torch.float16 else v.detach().cpu().numpy())
+                for k, v in t.items()}
         t0 = time.perf_counter()
-        kp, vp = oracle.kv_append(host["k_pool"], host["v_pool"], host["k_new"], host["v_new"], slots)
-        oracle.paged_attention(host["q"], kp, vp, wl.block_tables, wl.context_lens, qsl, wl.scale)
+        if kv_dtype == "fp8":
+            kc, vc, ks, vs = ofp8.kv_append(host["k_codes"], host["v_codes"], host["k_scale"],
+                                            host["v_scale"], host["k_new"], host["v_new"], slots)
+            oracle.paged_attention_fp8(host["q"], kc, vc, ks, vs, wl.block_tables,
+                                       wl.context_lens, qsl, wl.scale)
+        else:
+            kp, vp = oracle.kv_append(host["k_pool"], host["v_pool"], host["k_new"],
+                                      host["v_new"], slots)
+            oracle.paged_attention(host["q"], kp, vp, wl.block_tables, wl.context_lens, qsl,
+                                   wl.scale)
         spent += time.perf_counter() - t0
         layers += 1
         if spent >= budget_s:
@@ -234,8 +256,16 @@ def main():
     overrides = {k: v for k, v in (("layers", args.layers), ("batch", args.batch),
                                     ("ctx_len", args.ctx)) if v}
     wl = make(**overrides)
-    layers = [workloads.layer_tensors(wl, l, device="cuda") for l in range(wl.num_layers)]
-    caches = [pkv.KVCache(t["k_pool"], t["v_pool"]) for t in layers]
+    if args.kv_dtype == "fp8":
+        if not wl.short_chunk().all() or wl.num_decode_seqs < wl.num_seqs:
+            print(json.dumps({"error": "the fp8 cache serves decode steps only"}))
+            sys.exit(2)
+        layers = [workloads.layer_tensors_fp8(wl, l, device="cuda") for l in range(wl.num_layers)]
+        caches = [pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+                  for t in layers]
+    else:
+        layers = [workloads.layer_tensors(wl, l, device="cuda") for l in range(wl.num_layers)]
+        caches = [pkv.KVCache(t["k_pool"], t["v_pool"]) for t in layers]
     outs = [torch.empty_like(t["q"]) for t in layers]
     step = Step.from_workload(wl, kv_partition_tokens=args.partition,
                               use_schedule={"auto": None, "on": True, "off": False}[args.schedule])
@@ -300,19 +330,22 @@ def main():
     torch.cuda.synchronize()
     attn_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3 / wl.num_layers
 
-    alg_bytes = algorithmic_bytes_per_attention_launch(wl, fused)
+    alg_bytes = algorithmic_bytes_per_attention_launch(wl, fused, args.kv_dtype)
     achieved = alg_bytes / (attn_us * 1e-6) / 1e9
     copy_gbps = measured_copy_rate(alg_bytes)
     long_chunks = not wl.short_chunk().all()
     prefill = prefill_roofline(wl, caches, layers, outs) if long_chunks else None
     kv_bytes_step = (int(wl.context_lens[wl.short_chunk()].astype(np.int64).sum()) *
-                     wl.num_kv_heads * wl.head_dim * 2 * 2 * wl.num_layers)
+                     wl.num_kv_heads * kv_row_bytes(wl, args.kv_dtype) * 2 * wl.num_layers)
     multi = wl.num_decode_seqs < int(wl.short_chunk().sum())
     kernel = ("paged decode attention with the decode tokens' append fused in"
               if fused else "paged decode attention") + " (+ split-KV merge when split)"
     if multi:
         kernel += ("; multi-token decodes on the packed-row MFMA kernel (+ its merge)" +
                    (" after their append" if fused else ""))
+    if args.kv_dtype == "fp8":
+        kernel = ("paged decode attention over an fp8 (E4M3) cache (+ split-KV merge when split)" +
+                  ("; the step's rows quantized by the append kernel first" if fused else ""))
     result = {
         "metric": METRIC,
         "value": round(streamed_tokens(wl) / (ms_per_step * 1e-3), 1),
@@ -342,7 +375,10 @@ def main():
             "max_context": wl.max_context_len,
             "pool_blocks_per_layer": wl.num_blocks,
             "parallelism": "single-gpu",
-            "append": "fused into the decode kernel" if fused else "separate kernel",
+            "append": ("fused into the decode kernel" if args.kv_dtype == "fp16"
+                       else "quantizing append kernel in the same call") if fused
+                      else "separate kernel",
+            "kv_cache": "fp16" if args.kv_dtype == "fp16" else "fp8_e4m3 + fp32 row scales",
             "launch": "one HIP graph per step" if args.graph else "one library call per layer",
         },
         "roofline": {
@@ -351,7 +387,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl) if fused else None,
+            "traffic": measured_traffic(wl) if fused and args.kv_dtype == "fp16" else None,
             "kernel": kernel,
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
@@ -364,7 +400,7 @@ def main():
         result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
         result["prefill"] = prefill
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s)
+        result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s, args.kv_dtype)
     print(json.dumps(result), flush=True)
 
 

@@ -233,21 +233,15 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
-    // quantized cache: decode sequences only; the step's rows are appended
-    // (quantized) by the append kernel, then the decode kernel reads codes
+    // quantized cache: decode sequences only; with the append, the decode
+    // kernel quantizes and appends the step's rows itself
     if (num_prefill > 0) return PKV_ERR_UNSUPPORTED;
-    if (fused) {
-      rc = from_hip(pkv::launch_kv_append_fp8(
-          cache->k_pool, cache->v_pool, static_cast<float*>(cache->k_scale),
-          static_cast<float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
-          cache->head_dim, k_new, v_new, slot_mapping, num_tokens, s));
-      if (rc != PKV_OK) return rc;
-    }
+    const pkv::DecodeAppend app8{k_new, v_new, fused ? slot_mapping : nullptr};
     return from_hip(pkv::launch_paged_decode_fp8(
-        q, cache->k_pool, cache->v_pool, static_cast<const float*>(cache->k_scale),
-        static_cast<const float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
+        q, cache->k_pool, cache->v_pool, static_cast<float*>(cache->k_scale),
+        static_cast<float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
         num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq, context_lens,
-        num_decode_seqs, scale, plan, out, workspace, s));
+        num_decode_seqs, scale, plan, app8, out, workspace, s));
   }
   if (fused && num_tokens > num_decode_seqs) {
     // rows of the prefill chunks follow the decode rows

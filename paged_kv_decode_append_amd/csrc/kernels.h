@@ -62,12 +62,14 @@ hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, fl
                                 const int64_t* slot_mapping, int32_t num_tokens,
                                 hipStream_t stream);
 
-hipError_t launch_paged_decode_fp8(const void* q, const void* k_codes, const void* v_codes,
-                                   const float* k_scale, const float* v_scale,
-                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                                   int32_t head_dim, const int32_t* block_tables,
-                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                   int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+// With app.k_new set, the decode tokens are quantized and appended inside the
+// decode kernel (as with fp16).
+hipError_t launch_paged_decode_fp8(const void* q, void* k_codes, void* v_codes, float* k_scale,
+                                   float* v_scale, int64_t num_blocks, int32_t num_kv_heads,
+                                   int32_t num_q_heads, int32_t head_dim,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_decode_seqs,
+                                   float scale, const DecodePlan& plan, const DecodeAppend& app,
                                    void* out, void* workspace, hipStream_t stream);
 
 // Balanced decode schedule (decode_sched.hip): made once per step on the

@@ -68,6 +68,47 @@ __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t
 
 // ---------------------------------------------------------------- append ---
 
+// One fp16 row of D values quantized by one wave (lane l holds values
+// EPL*l .. EPL*l + EPL-1, EPL = D/64): returns the lane's EPL codes (byte k
+// of the word = value k) and sets e (the row's scale is 2^e).
+template <int D>
+__device__ __forceinline__ uint32_t quantize_row_wave(const uint16_t* __restrict__ row, int lane,
+                                                      int& e) {
+  constexpr int EPL = D / 64;
+  const uint16_t* src = row + EPL * lane;
+  float x[EPL];
+  if constexpr (EPL == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu));
+    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(src);
+    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x & 0xffffu));
+    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x >> 16));
+    x[2] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y & 0xffffu));
+    x[3] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y >> 16));
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  e = row_exponent(amax);
+  const float inv = exp2i(-e);  // exact scaling: |x * inv| <= 448
+  int c = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
+  if constexpr (EPL == 4) c = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, c, true);
+  return (uint32_t)c;
+}
+
+// Stores a lane's EPL codes (EPL = 2: two bytes; 4: four).
+template <int D>
+__device__ __forceinline__ void store_codes(uint8_t* dst, uint32_t c) {
+  if constexpr (D == 128)
+    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(c & 0xffffu);
+  else
+    *reinterpret_cast<uint32_t*>(dst) = c;
+}
+
 // One wave per (token, KV head) row of K (grid.y = 0) or V (grid.y = 1),
 // four rows per work-group; lane l quantizes values EPL*l .. EPL*l + EPL-1.
 template <int D>
@@ -88,36 +129,10 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
   if (b >= num_blocks) return;  // beyond the pool (a broken contract): skipped
   const int o = (int)(slot % kBlockSize);
   const bool is_v = blockIdx.y == 1;
-  const uint16_t* src = (is_v ? v_new : k_new) + r * D + EPL * lane;
-  float x[EPL];
-  if constexpr (EPL == 2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
-    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w & 0xffffu));
-    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w >> 16));
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(src);
-    x[0] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x & 0xffffu));
-    x[1] = (float)__builtin_bit_cast(f16, (uint16_t)(w.x >> 16));
-    x[2] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y & 0xffffu));
-    x[3] = (float)__builtin_bit_cast(f16, (uint16_t)(w.y >> 16));
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const int e = row_exponent(amax);
-  const float inv = exp2i(-e);  // exact scaling: |x * inv| <= 448
+  int e;
+  const uint32_t c = quantize_row_wave<D>((is_v ? v_new : k_new) + r * D, lane, e);
   const int64_t row = ((b * num_kv_heads + g) * kBlockSize + o);
-  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D + EPL * lane;
-  if constexpr (EPL == 2) {
-    const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
-    *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(c & 0xffffu);
-  } else {
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, c, true);
-    *reinterpret_cast<uint32_t*>(dst) = (uint32_t)c;
-  }
+  store_codes<D>((is_v ? v_codes : k_codes) + row * D + EPL * lane, c);
   if (lane == 0) (is_v ? v_scale : k_scale)[row] = exp2i(e);
 }
 
@@ -196,16 +211,35 @@ __device__ __forceinline__ void wave8_init(Wave8<D, G>& st) {
 // row scales, lazy-max online softmax, weights (times the V row scales over
 // the block's largest) to LDS as pairs of consecutive tokens; returns the
 // block's largest V scale (wave-uniform) for block_pv8.
+// knew: when not null, the codes of the K row appended in this step for
+// position ctx - 1 (LDS), with its K and V scales ksnew, vsnew; they replace
+// that row of the block holding ctx - 1.
 template <int D, int G>
-__device__ __forceinline__ float block_scores8(const KV8Regs<D>& r, const uint16_t* qs,
+__device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs,
                                                Wave8<D, G>& st, int tok0, int ctx,
                                                float scale_log2, uint32_t* __restrict__ p_lds,
+                                               const uint8_t* knew, float ksnew, float vsnew,
                                                int lane) {
   constexpr int GP = (G + 3) & ~3;
   static_assert(G <= 16, "one MFMA column per query head");
   const int row = lane & 15, grp = lane >> 4;
   const float kNegInf = -__builtin_huge_valf();
   asm volatile("" ::: "memory");  // re-read the query fragments from LDS every block
+  if (knew != nullptr && tok0 + 16 >= ctx) {
+    const int tn = ctx - 1 - tok0;
+    if (row == tn) {
+#pragma unroll
+      for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2)
+        r.k[c2] = *reinterpret_cast<const uint4*>(knew + 64 * c2 + 16 * grp);
+    }
+    if (grp == (tn >> 2)) {
+      const int i = tn & 3;
+      if (i == 0) { r.ks.x = ksnew; r.vs.x = vsnew; }
+      if (i == 1) { r.ks.y = ksnew; r.vs.y = vsnew; }
+      if (i == 2) { r.ks.z = ksnew; r.vs.z = vsnew; }
+      if (i == 3) { r.ks.w = ksnew; r.vs.w = vsnew; }
+    }
+  }
   const int hq = row < G ? row : 0;  // columns past G repeat head 0; masked below
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -271,14 +305,27 @@ __device__ __forceinline__ float block_scores8(const KV8Regs<D>& r, const uint16
   return vmax;
 }
 
+// vnew: when not null, the codes of the V row appended for position ctx - 1.
 template <int D, int G>
 __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int tok0, int ctx,
                                           const uint32_t* __restrict__ p_lds, float vmax,
-                                          int lane) {
+                                          const uint8_t* vnew, int lane) {
   constexpr int GP = (G + 3) & ~3;
   constexpr bool HALF = V8Layout<D>::HALF;
   constexpr int TOK = V8Layout<D>::TOK;
   const int base = HALF ? 8 * (lane >> 5) : 0;  // first token of this lane's v[]
+  if (vnew != nullptr && tok0 + 16 >= ctx) {
+    const int tn = ctx - 1 - tok0 - base;  // index in this lane's v[] (may be outside)
+    if (tn >= 0 && tn < TOK) {
+      // one bit per token, tested with constant j: keeps r.v in registers
+      const uint32_t hit = 1u << tn;
+      const uint32_t nv =
+          *reinterpret_cast<const uint32_t*>(vnew + 4 * (HALF ? (lane & 31) : lane));
+#pragma unroll
+      for (int j = 0; j < TOK; ++j)
+        if (hit & (1u << j)) r.v[j] = nv;
+    }
+  }
   // code 0 = +0 for rows past the context: stale rows never leak (a select on
   // every block, no branch: a branch around the buffer's registers would make
   // the compiler copy them and wait for every load in flight)
@@ -314,15 +361,25 @@ __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int to
   wave_fence();
 }
 
-template <int D, int G>
+// APPEND: the step's decode tokens are quantized and appended by this kernel
+// (as the fp16 kernel does): row i of k_new / v_new ([Hkv][D] fp16, one token
+// of sequence i) belongs at position ctx_i - 1.  The work-group whose
+// partition holds that position quantizes the rows into LDS at its start
+// (waves 0 and 1), uses them in place of the pool's row when slot_mapping[i]
+// is the table's slot of ctx_i - 1, and writes codes and scales to
+// slot_mapping[i] at its end (nothing when the slot is negative or beyond the
+// pool) -- the same result as the append kernel followed by the attention.
+template <int D, int G, bool APPEND>
 __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_codes,
-    const uint8_t* __restrict__ v_codes, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ q, uint8_t* __restrict__ k_codes,
+    uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
     const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
+  constexpr int EPL = D / 64;
   constexpr int GP = (G + 3) & ~3;
   // blocks in flight per wave: 16 KiB at d = 128 and at d = 256 up to G = 5
   // (larger groups keep one block, to stay within 256 registers)
@@ -332,6 +389,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   __shared__ float s_l[kWaves][G];
   __shared__ uint32_t s_p[kWaves][8 * GP];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
+  __shared__ __attribute__((aligned(16))) uint8_t s_newc[2][APPEND ? D : 16];  // K, V codes
+  __shared__ float s_news[2];                                                // their scales
 
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
@@ -353,6 +412,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) qstage[k] = qsrc[tid + 256 * k];
+  int64_t slot = -1;
+  if constexpr (APPEND) slot = slot_mapping[i];
 
   const int ctx = min(context_lens[i], ctx_clamp);
   const int nblk = (ctx + 15) >> 4;
@@ -384,7 +445,37 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
+  // The appended token sits in block nblk - 1; this partition holds it when
+  // nblk <= b1: its K (wave 0) and V (wave 1) rows quantized into LDS.
+  const bool owner = APPEND && nblk <= b1;
+  if constexpr (APPEND) {
+    if (owner && wave < 2) {
+      int e;
+      const uint32_t c = quantize_row_wave<D>(
+          (wave == 0 ? k_new : v_new) + ((int64_t)i * num_kv_heads + g) * D, lane, e);
+      store_codes<D>(&s_newc[wave][EPL * lane], c);
+      if (lane == 0) s_news[wave] = exp2i(e);
+    }
+  }
   __syncthreads();
+
+  // the wave that reads that block substitutes the rows
+  const uint8_t* knew = nullptr;
+  const uint8_t* vnew = nullptr;
+  float ksnew = 0.f, vsnew = 0.f;
+  if constexpr (APPEND) {
+    const int kl = nblk - 1 - b0 - wave;  // multiple of kWaves when this wave reads it
+    if (owner && kl >= 0 && kl % kWaves == 0 && slot >= 0) {
+      const uint32_t raw_last = (uint32_t)__builtin_amdgcn_readlane((int)raw_bid, kl / kWaves);
+      if (raw_last < (uint64_t)num_blocks &&
+          slot == (int64_t)raw_last * 16 + ((ctx - 1) & 15)) {
+        knew = s_newc[0];
+        vnew = s_newc[1];
+        ksnew = s_news[0];
+        vsnew = s_news[1];
+      }
+    }
+  }
 
   Wave8<D, G> st;
   wave8_init(st);
@@ -393,9 +484,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
       if (k + j >= nbw) break;
-      const float vmax =
-          block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2, s_p[wave], lane);
-      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, lane);
+      const float vmax = block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2,
+                                             s_p[wave], knew, ksnew, vsnew, lane);
+      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, vnew, lane);
       load_block(buf[j], k + j + NBUF);
     }
   }
@@ -449,15 +540,28 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
       }
     }
   }
+
+  // The appended rows to their slot (only this work-group reads the block
+  // that holds them, and it is done with it).
+  if constexpr (APPEND) {
+    if (owner && slot >= 0 && (slot >> 4) < num_blocks && wave < 2) {
+      const int64_t rowi = ((slot >> 4) * num_kv_heads + g) * 16 + (slot & 15);
+      const uint32_t c = EPL == 2 ? *reinterpret_cast<const uint16_t*>(&s_newc[wave][EPL * lane])
+                                  : *reinterpret_cast<const uint32_t*>(&s_newc[wave][EPL * lane]);
+      store_codes<D>((wave == 0 ? k_codes : v_codes) + rowi * D + EPL * lane, c);
+      if (lane == 0) (wave == 0 ? k_scale : v_scale)[rowi] = s_news[wave];
+    }
+  }
 }
 
-template <int D, int G>
-hipError_t launch_decode_fp8_dg(const void* q, const void* k_codes, const void* v_codes,
-                                const float* k_scale, const float* v_scale, int64_t num_blocks,
+template <int D, int G, bool APPEND>
+hipError_t launch_decode_fp8_dg(const void* q, void* k_codes, void* v_codes, float* k_scale,
+                                float* v_scale, int64_t num_blocks,
                                 int32_t num_kv_heads, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
                                 int32_t num_decode_seqs, float scale, const DecodePlan& plan,
-                                void* out, void* workspace, hipStream_t stream) {
+                                const DecodeAppend& app, void* out, void* workspace,
+                                hipStream_t stream) {
   const int32_t num_q_heads = num_kv_heads * G;
   const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
                                             (int64_t)plan.max_parts * plan.partition_blocks * 16);
@@ -466,14 +570,15 @@ hipError_t launch_decode_fp8_dg(const void* q, const void* k_codes, const void* 
   float* part_ml =
       part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
-  hipLaunchKernelGGL((paged_decode_fp8_kernel<D, G>),
+  hipLaunchKernelGGL((paged_decode_fp8_kernel<D, G, APPEND>),
                      dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
-                     stream, static_cast<const uint16_t*>(q),
-                     static_cast<const uint8_t*>(k_codes), static_cast<const uint8_t*>(v_codes),
-                     k_scale, v_scale, num_blocks, num_kv_heads, block_tables,
-                     max_blocks_per_seq, context_lens, ctx_clamp, plan.partition_blocks,
-                     plan.max_parts, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
-                     part_ml);
+                     stream, static_cast<const uint16_t*>(q), static_cast<uint8_t*>(k_codes),
+                     static_cast<uint8_t*>(v_codes), k_scale, v_scale, num_blocks,
+                     num_kv_heads, block_tables, max_blocks_per_seq, context_lens, ctx_clamp,
+                     plan.partition_blocks, plan.max_parts, scale * kLog2e,
+                     static_cast<uint16_t*>(out), part_o, part_ml,
+                     static_cast<const uint16_t*>(app.k_new),
+                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
   return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
@@ -481,15 +586,21 @@ hipError_t launch_decode_fp8_dg(const void* q, const void* k_codes, const void* 
 }
 
 template <int D>
-hipError_t launch_decode_fp8_d(int32_t group, const void* q, const void* kc, const void* vc,
-                               const float* ks, const float* vs, int64_t num_blocks,
-                               int32_t num_kv_heads, const int32_t* bt, int32_t maxblk,
-                               const int32_t* ctx, int32_t nseq, float scale,
-                               const DecodePlan& plan, void* out, void* ws, hipStream_t stream) {
-#define PKV_CASE(GG)                                                                        \
-  case GG:                                                                                 \
-    return launch_decode_fp8_dg<D, GG>(q, kc, vc, ks, vs, num_blocks, num_kv_heads, bt,    \
-                                       maxblk, ctx, nseq, scale, plan, out, ws, stream);
+hipError_t launch_decode_fp8_d(int32_t group, const void* q, void* kc, void* vc, float* ks,
+                               float* vs, int64_t num_blocks, int32_t num_kv_heads,
+                               const int32_t* bt, int32_t maxblk, const int32_t* ctx,
+                               int32_t nseq, float scale, const DecodePlan& plan,
+                               const DecodeAppend& app, void* out, void* ws,
+                               hipStream_t stream) {
+  const bool fused = app.k_new != nullptr;
+#define PKV_CASE(GG)                                                                          \
+  case GG:                                                                                   \
+    return fused ? launch_decode_fp8_dg<D, GG, true>(q, kc, vc, ks, vs, num_blocks,          \
+                                                     num_kv_heads, bt, maxblk, ctx, nseq,    \
+                                                     scale, plan, app, out, ws, stream)      \
+                 : launch_decode_fp8_dg<D, GG, false>(q, kc, vc, ks, vs, num_blocks,         \
+                                                      num_kv_heads, bt, maxblk, ctx, nseq,   \
+                                                      scale, plan, app, out, ws, stream);
   switch (group) {
     PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
     PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
@@ -524,25 +635,25 @@ hipError_t launch_kv_append_fp8(void* k_codes, void* v_codes, float* k_scale, fl
   return hipGetLastError();
 }
 
-hipError_t launch_paged_decode_fp8(const void* q, const void* k_codes, const void* v_codes,
-                                   const float* k_scale, const float* v_scale,
-                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                                   int32_t head_dim, const int32_t* block_tables,
-                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                   int32_t num_decode_seqs, float scale, const DecodePlan& plan,
+hipError_t launch_paged_decode_fp8(const void* q, void* k_codes, void* v_codes, float* k_scale,
+                                   float* v_scale, int64_t num_blocks, int32_t num_kv_heads,
+                                   int32_t num_q_heads, int32_t head_dim,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t* context_lens, int32_t num_decode_seqs,
+                                   float scale, const DecodePlan& plan, const DecodeAppend& app,
                                    void* out, void* workspace, hipStream_t stream) {
   if (num_decode_seqs == 0) return hipSuccess;
   const int32_t group = num_q_heads / num_kv_heads;
   if (head_dim == 128)
     return launch_decode_fp8_d<128>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
                                     num_kv_heads, block_tables, max_blocks_per_seq,
-                                    context_lens, num_decode_seqs, scale, plan, out, workspace,
-                                    stream);
+                                    context_lens, num_decode_seqs, scale, plan, app, out,
+                                    workspace, stream);
   if (head_dim == 256)
     return launch_decode_fp8_d<256>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
                                     num_kv_heads, block_tables, max_blocks_per_seq,
-                                    context_lens, num_decode_seqs, scale, plan, out, workspace,
-                                    stream);
+                                    context_lens, num_decode_seqs, scale, plan, app, out,
+                                    workspace, stream);
   return hipErrorInvalidValue;
 }
 

@@ -188,3 +188,32 @@ def test_full_size_fp8(name):
                                      wl.context_lens, None, wl.scale, seq_subset=subset)
     errs = assert_close(out.cpu().numpy()[subset], ref[subset], name)
     _report(f"{name} fp8 layer 3", errs)
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_fused_fp8_append_skips_a_padding_slot(part):
+    """A decode token with slot -1 is not written, and its sequence attends
+    the pool's current row at ctx - 1 -- as with the separate calls."""
+    ctx = [20, 40, 60, 300]
+    wl = workloads.custom("fp8_pad", ctx, [1] * 4, 4, 12, 2, 128, seed=37)
+    t = _fp8_cache(wl, poison=False)
+    kc0, vc0, ks0, vs0 = (_np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale"))
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, None, 16)
+    slots[1] = -1
+    slots[3] = -1
+    step = Step.from_workload(wl, kv_partition_tokens=part)
+    cache = pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+    out = torch.empty_like(t["q"])
+    pkv.append_attention_step(cache, t["k_new"], t["v_new"], torch.from_numpy(slots).cuda(),
+                              t["q"], out, step.block_tables, step.context_lens, None, 4,
+                              wl.scale, step.max_context_len, 1, workspace=step.workspace,
+                              kv_partition_tokens=part)
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = ofp8.kv_append(kc0, vc0, ks0, vs0, host_bits(t["k_new"]),
+                                    host_bits(t["v_new"]), slots)
+    assert np.array_equal(_np(t["k_codes"]), kc) and np.array_equal(_np(t["v_codes"]), vc)
+    assert np.array_equal(_np(t["k_scale"]).view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(_np(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, None, wl.scale)
+    _report(f"fp8 padding slot part={part}", assert_close(out.cpu().numpy(), ref, "fp8 pad"))

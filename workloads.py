@@ -225,22 +225,26 @@ def layer_tensors_fp8(wl: Workload, layer: int, device="cpu"):
     directly as bytes: k_codes, v_codes uint8 [NB, Hkv, 16, d] with random
     sign, exponent field 4..10 and mantissa (values 2^-3 .. ~15, no NaN
     codes), k_scale, v_scale float32 [NB, Hkv, 16] random powers of two
-    2^-6 .. 2^-3; plus fp16 q, k_new, v_new as layer_tensors.  Seeded by
-    (seed, layer)."""
+    2^-6 .. 2^-3; plus fp16 q, k_new, v_new as layer_tensors.  Drawn with a
+    torch generator seeded by (seed, layer) on `device`."""
     import torch
 
-    rng = np.random.default_rng([wl.seed, layer, 8])
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed * 1_000_003 + layer * 7919 + 29)
     shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
 
+    def randint(lo, hi, shp, dtype):
+        return torch.randint(lo, hi, shp, generator=gen, device=dev, dtype=dtype)
+
     def codes():
-        sign = rng.integers(0, 2, shape, dtype=np.uint8) << 7
-        expo = rng.integers(4, 11, shape, dtype=np.uint8) << 3
-        mant = rng.integers(0, 8, shape, dtype=np.uint8)
-        return torch.from_numpy(sign | expo | mant).to(device)
+        c = randint(0, 2, shape, torch.uint8) << 7
+        c |= randint(4, 11, shape, torch.uint8) << 3
+        c |= randint(0, 8, shape, torch.uint8)
+        return c
 
     def scales():
-        e = rng.integers(-6, -2, shape[:3])
-        return torch.from_numpy(np.ldexp(1.0, e).astype(np.float32)).to(device)
+        return torch.exp2(randint(-6, -2, shape[:3], torch.int32).to(torch.float32))
 
     t = layer_tensors(Workload(wl.name, wl.num_layers, wl.num_q_heads, wl.num_kv_heads,
                                wl.head_dim, wl.context_lens, wl.new_tokens, wl.num_decode_seqs,
