@@ -229,7 +229,7 @@ def cpu_baseline(wl, layer_tensors_dev, budget_s: float, kv_dtype: str = "fp16")
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "one GPU only: the benchmark measures a single device; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
