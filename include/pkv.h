@@ -259,6 +259,10 @@ int pkv_decode_schedule(const int32_t* context_lens, int32_t num_decode_seqs,
  * num_q_heads / num_kv_heads <= 64, e.g. a decoding sequence verifying a few
  * drafted tokens) with all query heads of a KV head packed into one
  * work-group; all on `stream`.
+ * Over an fp8 cache the decode part always uses the partition grid (the
+ * schedule is ignored), and the prefill kernel turns the codes it stages
+ * into fp16 (exact) and applies the row scales to the scores (K) and to the
+ * softmax weights (V); the result is attention over the dequantized cache.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE,
  * PKV_ERR_HIP.
  */
@@ -286,7 +290,8 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
  * position ctx_i - 1 takes the new row from k_new / v_new instead of the
  * pool and writes it to slot_mapping[i] at its end.  Prefill tokens (rows
  * num_decode_seqs .. num_tokens-1) are appended by the append kernel before
- * the prefill kernel runs.
+ * the prefill kernel runs.  Over an fp8 cache both quantize the rows as
+ * pkv_kv_append does.
  *
  *   k_new, v_new   device fp16 [num_tokens][num_kv_heads][head_dim]
  *   slot_mapping   device int64 [num_tokens]; as for pkv_kv_append.  The

@@ -233,15 +233,33 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
-    // quantized cache: decode sequences only; with the append, the decode
-    // kernel quantizes and appends the step's rows itself
-    if (num_prefill > 0) return PKV_ERR_UNSUPPORTED;
+    // quantized cache (partition grid only): with the append, the prefill
+    // rows are quantized by the append kernel ahead of the attention, and
+    // the decode kernel quantizes and appends the decode rows itself
+    float* k_scale = static_cast<float*>(cache->k_scale);
+    float* v_scale = static_cast<float*>(cache->v_scale);
+    if (fused && num_tokens > num_decode_seqs) {
+      const size_t row_bytes = (size_t)cache->num_kv_heads * cache->head_dim * 2;
+      rc = from_hip(pkv::launch_kv_append_fp8(
+          cache->k_pool, cache->v_pool, k_scale, v_scale, cache->num_blocks,
+          cache->num_kv_heads, cache->head_dim,
+          static_cast<const char*>(k_new) + (size_t)num_decode_seqs * row_bytes,
+          static_cast<const char*>(v_new) + (size_t)num_decode_seqs * row_bytes,
+          slot_mapping + num_decode_seqs, num_tokens - num_decode_seqs, s));
+      if (rc != PKV_OK) return rc;
+    }
     const pkv::DecodeAppend app8{k_new, v_new, fused ? slot_mapping : nullptr};
-    return from_hip(pkv::launch_paged_decode_fp8(
-        q, cache->k_pool, cache->v_pool, static_cast<float*>(cache->k_scale),
-        static_cast<float*>(cache->v_scale), cache->num_blocks, cache->num_kv_heads,
-        num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq, context_lens,
-        num_decode_seqs, scale, plan, app8, out, workspace, s));
+    rc = from_hip(pkv::launch_paged_decode_fp8(
+        q, cache->k_pool, cache->v_pool, k_scale, v_scale, cache->num_blocks,
+        cache->num_kv_heads, num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq,
+        context_lens, num_decode_seqs, scale, plan, app8, out, workspace, s));
+    if (rc != PKV_OK) return rc;
+    return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, k_scale, v_scale,
+                                        cache->num_blocks, cache->num_kv_heads, num_q_heads,
+                                        cache->head_dim, block_tables, max_blocks_per_seq,
+                                        context_lens, query_start_loc, num_decode_seqs,
+                                        num_prefill, max_query_len, scale, pplan, out,
+                                        prefill_ws, s));
   }
   if (fused && num_tokens > num_decode_seqs) {
     // rows of the prefill chunks follow the decode rows
@@ -265,11 +283,12 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
         cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
         plan, app, out, workspace, s));
   if (rc != PKV_OK) return rc;
-  return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, cache->num_blocks,
-                                      cache->num_kv_heads, num_q_heads, cache->head_dim,
-                                      block_tables, max_blocks_per_seq, context_lens,
-                                      query_start_loc, num_decode_seqs, num_prefill,
-                                      max_query_len, scale, pplan, out, prefill_ws, s));
+  return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, nullptr, nullptr,
+                                      cache->num_blocks, cache->num_kv_heads, num_q_heads,
+                                      cache->head_dim, block_tables, max_blocks_per_seq,
+                                      context_lens, query_start_loc, num_decode_seqs,
+                                      num_prefill, max_query_len, scale, pplan, out,
+                                      prefill_ws, s));
 }
 
 }  // namespace

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
-  constexpr int LPT = D / 16, EPL = D / 64, GP = (G + 3) & ~3;
+  constexpr int GP = (G + 3) & ~3;
   // d = 128: two blocks (16 KiB) in flight per wave by refilling a buffer as
   // soon as each half is consumed; d = 256: one block is already 16 KiB, and
   // the plain two-buffer scheme keeps registers under 256 (2 waves per SIMD).
@@ -280,49 +280,95 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
 }
 
 // One work-group per (sequence, query head) with more than one partition:
-// the 4 waves take every 4th partition, then combine through LDS.
+//   M = max_p m_p,  w_p = l_p 2^(m_p - M),  O = sum_p w_p o_p / sum_p w_p.
+// The merge sits between two kernels on the step's critical path, so its
+// memory round trips are what it costs: the context length and the (m, l)
+// pairs are requested together (thread p holds pair p; pairs past the
+// sequence's partition count are stale and selected away), and the first
+// kMergeUnroll partitions of each wave's o vectors (wave w takes every 4th
+// partition from w) are in flight while M is reduced.
+constexpr int kMergeUnroll = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, int32_t num_q_heads, uint16_t* __restrict__ out) {
   constexpr int EPL = D / 64;
+  constexpr int kStride = 4 * kMergeUnroll;  // partitions per round of the 4 waves
   __shared__ float s_max[4];
-  __shared__ float s_w[4];
+  __shared__ float s_w[256];
+  __shared__ float s_wsum[4];
   __shared__ float s_acc[4][D];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int row_head = blockIdx.x;
   const int i = row_head / num_q_heads;
-  const int nblk = (min(context_lens[i], ctx_clamp) + 15) >> 4;
-  const int np = (nblk + partition_blocks - 1) / partition_blocks;
-  if (np <= 1) return;  // written directly by the decode kernel
   const float* ml = part_ml + (int64_t)row_head * max_parts * 2;
   const float* po = part_o + (int64_t)row_head * max_parts * D + EPL * lane;
+  const int ctx = context_lens[i];
+  float2 own = {-__builtin_huge_valf(), 0.f};
+  if (tid < max_parts) own = *reinterpret_cast<const float2*>(ml + 2 * tid);
+  const int nblk = (min(ctx, ctx_clamp) + 15) >> 4;
+  const int np = (nblk + partition_blocks - 1) / partition_blocks;
+  if (np <= 1) return;  // written directly by the decode kernel
 
-  float M = -__builtin_huge_valf();
-  for (int p = tid; p < np; p += 256) M = fmaxf(M, ml[2 * p]);
+  // Every partition p < np holds at least one position: m_p is finite,
+  // l_p > 0, o_p written.  Loads of p >= np re-read partition np - 1.
+  float v[kMergeUnroll][EPL];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const int pc = min(wave + 4 * u, np - 1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)pc * D + e];
+  }
+
+  float M = tid < np ? own.x : -__builtin_huge_valf();
+  for (int p = tid + 256; p < np; p += 256) M = fmaxf(M, ml[2 * p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   if (lane == 0) s_max[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+  s_w[tid] = tid < np ? own.y * fast_exp2(own.x - M) : 0.f;
+  __syncthreads();
+  auto weight = [&](int p) -> float {
+    if (p >= np) return 0.f;
+    if (p < 256) return s_w[p];
+    return ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+  };
 
   float W = 0.f, acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll 4
-  for (int p = wave; p < np; p += 4) {
-    const float w = ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const float w = weight(wave + 4 * u);
     W += w;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * po[(int64_t)p * D + e];
+    for (int e = 0; e < EPL; ++e) acc[e] += w * v[u][e];
+  }
+  // more partitions than one round holds (long contexts)
+  for (int p0 = wave + kStride; p0 < np; p0 += kStride) {
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int pc = min(p0 + 4 * u, np - 1);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)pc * D + e];
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float w = weight(p0 + 4 * u);
+      W += w;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += w * v[u][e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) s_acc[wave][EPL * lane + e] = acc[e];
-  if (lane == 0) s_w[wave] = W;
+  if (lane == 0) s_wsum[wave] = W;
   __syncthreads();
   if (tid < D) {
-    const float total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    const float total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
     const float o = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
     out[(int64_t)row_head * D + tid] = __builtin_bit_cast(uint16_t, (f16)(o / total));
   }

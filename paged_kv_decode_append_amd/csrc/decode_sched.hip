@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int64_t* __restrict__ slot_mapping) {
-  constexpr int LPT = D / 16, EPL = D / 64, GP = (G + 3) & ~3, RCH = D / 8;
+  constexpr int GP = (G + 3) & ~3, RCH = D / 8;
   constexpr bool kEarlyRefill = D == 128;
   constexpr int QCH = G * D / 8;
   constexpr int QPT = (QCH + 255) / 256;  // query chunks per thread

@@ -113,14 +113,15 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
                          int32_t kv_partition_tokens);
 
 // Causal attention of the prefill chunks (sequences first_seq ..
-// first_seq + num_prefill_seqs - 1) on the matrix cores.
+// first_seq + num_prefill_seqs - 1) on the matrix cores.  With k_scale set
+// the pools hold fp8 (E4M3) codes and k_scale / v_scale their row scales.
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
-                          int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                          int32_t head_dim, const int32_t* block_tables,
-                          int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          const int32_t* query_start_loc, int32_t first_seq,
-                          int32_t num_prefill_seqs, int32_t max_query_len, float scale,
-                          const PrefillPlan& plan, void* out, void* workspace,
+                          const float* k_scale, const float* v_scale, int64_t num_blocks,
+                          int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, const int32_t* query_start_loc,
+                          int32_t first_seq, int32_t num_prefill_seqs, int32_t max_query_len,
+                          float scale, const PrefillPlan& plan, void* out, void* workspace,
                           hipStream_t stream);
 
 }  // namespace pkv

@@ -42,6 +42,7 @@
 #include <climits>
 
 #include "device_util.h"
+#include "fp8_util.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -137,12 +138,6 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
 }
 
 // ---------------------------------------------------------------- decode ---
-
-// Two E4M3 codes (bytes 0-1 when hi is false, 2-3 when true) to an fp16 pair.
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_h2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
-}
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

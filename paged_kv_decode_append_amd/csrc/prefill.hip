@@ -38,6 +38,7 @@
 #include <climits>
 
 #include "device_util.h"
+#include "fp8_util.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -77,11 +78,21 @@ struct PrefillShape {
   static constexpr int kIdTiles = 64;            // tiles whose block ids are staged in LDS
 };
 
-// One thread's share of a K/V tile in flight: 4 K chunks of 16 bytes, and
-// 4 tokens x 8 d values of V (one 4x8 group per thread).
+// One thread's share of a K/V tile in flight.  fp16 cache: 4 K chunks of 8
+// values, and 4 tokens x 8 d values of V (one 4x8 group per thread).  fp8
+// cache: the same tokens and columns as codes (2 K chunks of 16, 4 x 8 V
+// codes), and one row scale (threads 0 .. KT-1: K of token tid, KT .. 2KT-1:
+// V of token tid - KT).
+template <bool FP8>
 struct TileRegs {
   uint4 k[4];
   uint4 v[4];
+};
+template <>
+struct TileRegs<true> {
+  uint4 k[2];
+  uint2 v[4];
+  float sc;
 };
 
 // HPW query heads of one KV group per wave (its 16 rows of each): every K
@@ -89,10 +100,11 @@ struct TileRegs {
 // needs ~350 registers (one wave per SIMD) and runs slower than HPW = 1 at
 // three waves per SIMD, whose waves hide each other's MFMA, LDS and exp
 // latencies; only HPW = 1 is launched.
-template <int D, int HPW, bool PACK>
+template <int D, int HPW, bool PACK, bool FP8>
 __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGroupsPerCU256) : 1) void prefill_chunk_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pool,
-    const uint16_t* __restrict__ v_pool, int64_t num_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ q, const void* __restrict__ k_pool_raw,
+    const void* __restrict__ v_pool_raw, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
     int32_t num_q_heads, const int32_t* __restrict__ block_tables, int32_t max_blocks_per_seq,
     const int32_t* __restrict__ context_lens, const int32_t* __restrict__ query_start_loc,
     int32_t first_seq, int32_t ctx_clamp, int32_t num_splits, int32_t split_tiles,
@@ -104,6 +116,12 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   static_assert(!PACK || HPW == 1, "packed rows carry their own head");
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_BYTES / 2];
   __shared__ int64_t s_tile_base[S::kIdTiles * (KT / 16)];  // pool offsets of staged blocks
+  // fp8: the tile's row scales, K then V (0 for tokens past pos_hi)
+  __shared__ __attribute__((aligned(16))) float s_scale[FP8 ? 2 * KT : 4];
+  const uint16_t* __restrict__ k_pool = static_cast<const uint16_t*>(k_pool_raw);
+  const uint16_t* __restrict__ v_pool = static_cast<const uint16_t*>(v_pool_raw);
+  const uint8_t* __restrict__ k_codes = static_cast<const uint8_t*>(k_pool_raw);
+  const uint8_t* __restrict__ v_codes = static_cast<const uint8_t*>(v_pool_raw);
   uint16_t* k_lds = lds;                         // [KT][KSTRIDE]
   uint16_t* vt_lds = lds + KT * S::KSTRIDE;      // [D][VSTRIDE]
 
@@ -198,7 +216,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   }
   __syncthreads();
   // Global -> registers for tile kt; tokens past pos_hi are zeros.
-  auto load_tile = [&](TileRegs& r, int kt) {
+  auto load_tile = [&](TileRegs<FP8>& r, int kt) {
     const int tok0 = kt * KT;
     int64_t tile_base[KT / 16];
 #pragma unroll
@@ -206,38 +224,85 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
       const int e = (kt - kt_begin) * (KT / 16) + b;
       tile_base[b] = e < S::kIdTiles * (KT / 16) ? s_tile_base[e] : block_base(kt * (KT / 16) + b);
     }
+    if constexpr (FP8) {
+      // codes: element offsets are byte offsets; a row's scale sits at its
+      // element offset / D
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      const int tok = idx / (D / 8), ch = idx % (D / 8);
-      r.k[j] = uint4{0u, 0u, 0u, 0u};
-      if (tok0 + tok <= pos_hi)
-        r.k[j] = *reinterpret_cast<const uint4*>(k_pool + tile_base[tok >> 4] +
-                                                 (tok & 15) * D + 8 * ch);
-    }
-    const int tq = tid % (KT / 4), dg = tid / (KT / 4);
+      for (int j = 0; j < 2; ++j) {
+        const int idx = tid + 256 * j;
+        const int tok = idx / (D / 16), ch = idx % (D / 16);
+        r.k[j] = uint4{0u, 0u, 0u, 0u};
+        if (tok0 + tok <= pos_hi)
+          r.k[j] = *reinterpret_cast<const uint4*>(k_codes + tile_base[tok >> 4] +
+                                                   (tok & 15) * D + 16 * ch);
+      }
+      const int tq = tid % (KT / 4), dg = tid / (KT / 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int tok = 4 * tq + t;
-      r.v[t] = uint4{0u, 0u, 0u, 0u};
-      if (tok0 + tok <= pos_hi)
-        r.v[t] = *reinterpret_cast<const uint4*>(v_pool + tile_base[tok >> 4] + (tok & 15) * D +
-                                                 8 * dg);
+      for (int t = 0; t < 4; ++t) {
+        const int tok = 4 * tq + t;
+        r.v[t] = uint2{0u, 0u};
+        if (tok0 + tok <= pos_hi)
+          r.v[t] = *reinterpret_cast<const uint2*>(v_codes + tile_base[tok >> 4] +
+                                                   (tok & 15) * D + 8 * dg);
+      }
+      r.sc = 0.f;
+      const int stok = tid % KT;
+      if (tid < 2 * KT && tok0 + stok <= pos_hi)
+        r.sc = (tid < KT ? k_scale : v_scale)[tile_base[stok >> 4] / D + (stok & 15)];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        const int tok = idx / (D / 8), ch = idx % (D / 8);
+        r.k[j] = uint4{0u, 0u, 0u, 0u};
+        if (tok0 + tok <= pos_hi)
+          r.k[j] = *reinterpret_cast<const uint4*>(k_pool + tile_base[tok >> 4] +
+                                                   (tok & 15) * D + 8 * ch);
+      }
+      const int tq = tid % (KT / 4), dg = tid / (KT / 4);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tok = 4 * tq + t;
+        r.v[t] = uint4{0u, 0u, 0u, 0u};
+        if (tok0 + tok <= pos_hi)
+          r.v[t] = *reinterpret_cast<const uint4*>(v_pool + tile_base[tok >> 4] + (tok & 15) * D +
+                                                   8 * dg);
+      }
     }
   };
   // Registers -> LDS: K row-major, V transposed to [d][token] (4x8 transpose).
-  auto store_tile = [&](const TileRegs& r) {
+  // fp8: codes are turned into fp16 here (exact), so the tiles in LDS and
+  // the MFMAs are those of the fp16 cache; the row scales go to s_scale.
+  auto store_tile = [&](const TileRegs<FP8>& r) {
+    uint4 vh[4];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int idx = tid + 256 * j;
-      const int tok = idx / (D / 8), ch = idx % (D / 8);
-      *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 8 * ch) = r.k[j];
+      for (int j = 0; j < 2; ++j) {
+        const int idx = tid + 256 * j;
+        const int tok = idx / (D / 16), ch = idx % (D / 16);
+        uint4 lo, hi;
+        fp8x16_to_h16(r.k[j], lo, hi);
+        *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 16 * ch) = lo;
+        *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 16 * ch + 8) = hi;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vh[t] = fp8x8_to_h8(r.v[t]);
+      if (tid < 2 * KT) s_scale[tid] = r.sc;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = tid + 256 * j;
+        const int tok = idx / (D / 8), ch = idx % (D / 8);
+        *reinterpret_cast<uint4*>(k_lds + tok * S::KSTRIDE + 8 * ch) = r.k[j];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vh[t] = r.v[t];
     }
     const int tq = tid % (KT / 4), dg = tid / (KT / 4);
-    const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-    const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-    const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
-    const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+    const uint32_t w0[4] = {vh[0].x, vh[0].y, vh[0].z, vh[0].w};
+    const uint32_t w1[4] = {vh[1].x, vh[1].y, vh[1].z, vh[1].w};
+    const uint32_t w2[4] = {vh[2].x, vh[2].y, vh[2].z, vh[2].w};
+    const uint32_t w3[4] = {vh[3].x, vh[3].y, vh[3].z, vh[3].w};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int w = j >> 1;
@@ -253,7 +318,11 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     }
   };
 
-  TileRegs next;
+  // fp8: O is kept in units of vref, the largest V row scale seen so far (a
+  // power of two; O is rescaled when a tile brings a larger one), so that
+  // every fp16 weight p 2^(e_t) / vref stays <= p
+  float vref = 0.f, inv_vref = 0.f;
+  TileRegs<FP8> next;
   if (kt_begin < kt_end) load_tile(next, kt_begin);
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int tok0 = kt * KT;
@@ -276,6 +345,45 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) s[hh][t] = mfma16(a, qb[hh][c], s[hh][t]);
       }
+    }
+    // fp8: scores times the K row scales (exact: powers of two); the V row
+    // scales of this lane's tokens relative to vref
+    float vrel[NT][4];
+    if constexpr (FP8) {
+      float vmax = 0.f;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float4 ks = *reinterpret_cast<const float4*>(s_scale + 16 * t + 4 * lgrp);
+        const float4 vs = *reinterpret_cast<const float4*>(s_scale + KT + 16 * t + 4 * lgrp);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          s[hh][t][0] *= ks.x;
+          s[hh][t][1] *= ks.y;
+          s[hh][t][2] *= ks.z;
+          s[hh][t][3] *= ks.w;
+        }
+        vrel[t][0] = vs.x;
+        vrel[t][1] = vs.y;
+        vrel[t][2] = vs.z;
+        vrel[t][3] = vs.w;
+        vmax = fmaxf(fmaxf(vmax, fmaxf(vs.x, vs.y)), fmaxf(vs.z, vs.w));
+      }
+      // lanes of one lgrp hold the same tokens; the four groups cover the tile
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+      if (vmax > vref) {  // the same in every lane and wave
+        const float ratio = vref / vmax;  // exact: powers of two (0 before the first tile)
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+          for (int t = 0; t < DT; ++t) o[hh][t] *= ratio;
+        vref = vmax;
+        inv_vref = 1.f / vmax;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vrel[t][e] *= inv_vref;
     }
 
     // Online softmax per (head, row), base 2.  Off the diagonal every token
@@ -338,6 +446,9 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
           const float p1 = fast_exp2(__builtin_fmaf(sv[2 * (j % 2) + 1], sc, neg_ref));
           w[j] = pack_h2_rtz(p0, p1);
           l_row[hh] = dot2(w[j], kOnesH2, l_row[hh]);
+          if constexpr (FP8)  // the same rounded weights, times 2^(e_t) / vref
+            w[j] = pack_h2_rtz(p0 * vrel[2 * c2 + j / 2][2 * (j % 2)],
+                               p1 * vrel[2 * c2 + j / 2][2 * (j % 2) + 1]);
         }
         pb[hh][c2] = __builtin_bit_cast(f16x8, uint4{w[0], w[1], w[2], w[3]});
       }
@@ -368,7 +479,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   const int64_t first_row = query_start_loc[first_seq];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const float inv = l_row[hh] > 0.f ? 1.f / l_row[hh] : 0.f;
+    const float inv = l_row[hh] > 0.f ? (FP8 ? vref : 1.f) / l_row[hh] : 0.f;
     const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + my_head + hh;
     if (num_splits == 1) {
       uint16_t* dst = out + row_head * D + 4 * lgrp;
@@ -490,9 +601,9 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
   return plan;
 }
 
-template <int D>
+template <int D, bool FP8>
 static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void* v_pool,
-                                   int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
+                                   const float* k_scale, const float* v_scale, int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                                    const int32_t* context_lens, const int32_t* query_start_loc,
                                    int32_t first_seq, int32_t num_prefill_seqs,
@@ -506,9 +617,9 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
   if (plan.packed) {
     // x = split, y = KV head: each work-group holds all heads of its group
     const dim3 grid((uint32_t)plan.splits, num_kv_heads, num_prefill_seqs);
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, true>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, true, FP8>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), k_pool, v_pool, k_scale, v_scale,
+                       num_blocks, num_kv_heads,
                        num_q_heads, block_tables, max_blocks_per_seq, context_lens,
                        query_start_loc, first_seq, ctx_clamp, plan.splits, plan.split_tiles,
                        scale * kLog2e,
@@ -520,9 +631,9 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
     // reads the K/V tiles through the same L2.
     const uint32_t x = ((max_query_len + kRows - 1) / kRows) * plan.splits;
     const dim3 grid((x + kXcds - 1) / kXcds * kXcds, num_q_heads, num_prefill_seqs);
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, false>), grid, dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_pool),
-                       static_cast<const uint16_t*>(v_pool), num_blocks, num_kv_heads,
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, 1, false, FP8>), grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(q), k_pool, v_pool, k_scale, v_scale,
+                       num_blocks, num_kv_heads,
                        num_q_heads, block_tables, max_blocks_per_seq, context_lens,
                        query_start_loc, first_seq, ctx_clamp, plan.splits, plan.split_tiles,
                        scale * kLog2e,
@@ -539,24 +650,26 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
 }
 
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
-                          int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
-                          int32_t head_dim, const int32_t* block_tables,
-                          int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          const int32_t* query_start_loc, int32_t first_seq,
-                          int32_t num_prefill_seqs, int32_t max_query_len, float scale,
-                          const PrefillPlan& plan, void* out, void* workspace,
+                          const float* k_scale, const float* v_scale, int64_t num_blocks,
+                          int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, const int32_t* query_start_loc,
+                          int32_t first_seq, int32_t num_prefill_seqs, int32_t max_query_len,
+                          float scale, const PrefillPlan& plan, void* out, void* workspace,
                           hipStream_t stream) {
   if (num_prefill_seqs <= 0) return hipSuccess;
+  const bool fp8 = k_scale != nullptr;
+#define PKV_PREFILL_ARGS                                                                      \
+  q, k_pool, v_pool, k_scale, v_scale, num_blocks, num_kv_heads, num_q_heads, block_tables,  \
+      max_blocks_per_seq, context_lens, query_start_loc, first_seq, num_prefill_seqs,         \
+      max_query_len, scale, plan, out, workspace, stream
   if (head_dim == 128)
-    return launch_prefill_d<128>(q, k_pool, v_pool, num_blocks, num_kv_heads, num_q_heads,
-                                 block_tables, max_blocks_per_seq, context_lens,
-                                 query_start_loc, first_seq, num_prefill_seqs, max_query_len,
-                                 scale, plan, out, workspace, stream);
+    return fp8 ? launch_prefill_d<128, true>(PKV_PREFILL_ARGS)
+               : launch_prefill_d<128, false>(PKV_PREFILL_ARGS);
   if (head_dim == 256)
-    return launch_prefill_d<256>(q, k_pool, v_pool, num_blocks, num_kv_heads, num_q_heads,
-                                 block_tables, max_blocks_per_seq, context_lens,
-                                 query_start_loc, first_seq, num_prefill_seqs, max_query_len,
-                                 scale, plan, out, workspace, stream);
+    return fp8 ? launch_prefill_d<256, true>(PKV_PREFILL_ARGS)
+               : launch_prefill_d<256, false>(PKV_PREFILL_ARGS);
+#undef PKV_PREFILL_ARGS
   return hipErrorInvalidValue;
 }
 

@@ -164,29 +164,104 @@ def test_step_appends_quantized_rows_then_attends(fused):
     _report(f"fp8 step fused={fused}", assert_close(out.cpu().numpy(), ref, "fp8 step"))
 
 
-def test_prefill_chunks_over_an_fp8_cache_are_refused():
-    wl = workloads.custom("fp8_chunk", [40, 20], [1, 8], 1, 12, 2, 128, seed=31)
-    t = _fp8_cache(wl, poison=False)
-    with pytest.raises(pkv.PkvError) as e:
-        _run(wl, t)
-    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+def _append_ref(wl, t0, t):
+    """The oracle's append replay of the step's rows over the pre-step pools
+    t0 (host copies); checks the GPU pools (codes and scales) bit for bit."""
+    qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, 16)
+    kc, vc, ks, vs = ofp8.kv_append(t0["k_codes"], t0["v_codes"], t0["k_scale"], t0["v_scale"],
+                                    host_bits(t["k_new"]), host_bits(t["v_new"]), slots)
+    assert np.array_equal(_np(t["k_codes"]), kc) and np.array_equal(_np(t["v_codes"]), vc)
+    assert np.array_equal(_np(t["k_scale"]).view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(_np(t["v_scale"]).view(np.uint32), vs.view(np.uint32))
+    return kc, vc, ks, vs, qsl
 
 
-@pytest.mark.parametrize("name", ["qwen_uniform", "qwen_ragged"])
+FP8_CHUNKS = {
+    # decodes, then short chunks whose G x n rows fit one tile (packed rows),
+    # crossing block edges, one over a long cached context
+    "short": ([15, 16, 17, 33, 40, 16, 17, 33, 8, 300, 1500], [1, 1, 1, 1, 8, 8, 3, 5, 8, 4, 2], 4),
+    # chunks longer than a 64-row tile, with and without a cached prefix
+    "long": ([300, 100, 64, 65, 500, 2100], [1, 100, 64, 65, 130, 200], 1),
+}
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("kind", ["short", "long"])
+@pytest.mark.parametrize("d,hq,hkv", [(128, 12, 2), (128, 8, 8), (256, 16, 4), (256, 24, 3)])
+def test_chunks_over_an_fp8_cache(d, hq, hkv, kind, fused):
+    """Prefill chunks (and decodes) in one step over an fp8 cache: the rows
+    quantized into their slots bit-exactly, then every query row within
+    tolerance of the oracle over the dequantized cache."""
+    ctx, new, ndec = FP8_CHUNKS[kind]
+    wl = workloads.custom(f"fp8_{kind}", ctx, new, ndec, hq, hkv, d, seed=hq * d + len(kind))
+    t = _fp8_cache(wl)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, fused=fused)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    errs = assert_close(out.cpu().numpy(), ref, f"fp8 {kind} chunks d={d} G={hq // hkv}")
+    _report(f"fp8 {kind} chunks d={d} G={hq // hkv} fused={fused}", errs)
+
+
+@pytest.mark.parametrize("part", [64, 256])
+def test_short_chunk_splits_over_an_fp8_cache(part):
+    """Packed short chunks with the context cut into fixed splits (merged by
+    log-sum-exp), some splits empty for the short contexts."""
+    ctx = [16, 100, 700, 1500, 3000]
+    wl = workloads.custom("fp8_spec", ctx, [4] * len(ctx), 0, 12, 2, 128, seed=part)
+    t = _fp8_cache(wl)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, part=part, fused=True)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    _report(f"fp8 short chunks part={part}",
+            assert_close(out.cpu().numpy(), ref, f"fp8 short chunks part={part}"))
+
+
+def test_qwen_mixed_full_size_fp8():
+    """64 decodes + a 512-row chunk over an 8,192-token prefix over an fp8
+    cache: sampled decode sequences, and chunk rows sampled across all 8 row
+    tiles, each checked as the query attending positions [0, its position]."""
+    wl = workloads.qwen_mixed()
+    t = _fp8_cache(wl, layer=5, poison=False)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, fused=True)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    got, q = out.cpu().numpy(), host_bits(t["q"])
+    subset = [0, 17, 40, 63]
+    ref = oracle.paged_attention_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.context_lens, qsl,
+                                     wl.scale, seq_subset=subset)
+    errs = assert_close(got[subset], ref[subset], "qwen_mixed fp8 decodes")
+    seq = wl.num_seqs - 1
+    rows = np.array([0, 1, 15, 16, 63, 64, 127, 200, 255, 256, 300, 383, 448, 500, 510, 511])
+    n, ctx, r0 = wl.new_tokens[seq], wl.context_lens[seq], wl.query_start_loc[seq]
+    sub_ctx = (ctx - n + rows + 1).astype(np.int32)
+    sub_bt = np.repeat(wl.block_tables[seq:seq + 1], len(rows), axis=0)
+    sub_ref = oracle.paged_attention_fp8(q[r0 + rows], kc, vc, ks, vs, sub_bt, sub_ctx, None,
+                                         wl.scale)
+    e2 = assert_close(got[r0 + rows], sub_ref, "qwen_mixed fp8 chunk rows")
+    _report("qwen_mixed fp8 layer 5", (max(errs[0], e2[0]), max(errs[1], e2[1])))
+
+
+@pytest.mark.parametrize("name", ["qwen_uniform", "qwen_ragged", "qwen_spec"])
 def test_full_size_fp8(name):
-    """One layer of the 28-layer workloads over an fp8 cache, sampled
+    """One layer of the 28-layer workloads over an fp8 cache (qwen_spec:
+    64 sequences verifying 4 tokens each, on the packed-row kernel), sampled
     sequences against the oracle."""
     wl = workloads.WORKLOADS[name]()
     t = _fp8_cache(wl, layer=3, poison=False)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
     _, out = _run(wl, t, fused=True)
-    kc, vc, ks, vs = ofp8.kv_append(*(_np(t[n]) for n in ("k_codes", "v_codes", "k_scale",
-                                                          "v_scale")),
-                                    host_bits(t["k_new"]), host_bits(t["v_new"]),
-                                    oracle.slot_mapping(wl.block_tables, wl.context_lens, None, 16))
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
     subset = [0, 1, 17, 40, wl.num_seqs - 1]
     ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
-                                     wl.context_lens, None, wl.scale, seq_subset=subset)
-    errs = assert_close(out.cpu().numpy()[subset], ref[subset], name)
+                                     wl.context_lens, qsl, wl.scale, seq_subset=subset)
+    rows = np.concatenate([np.arange(wl.query_start_loc[i], wl.query_start_loc[i + 1])
+                           for i in subset])
+    errs = assert_close(out.cpu().numpy()[rows], ref[rows], name)
     _report(f"{name} fp8 layer 3", errs)
 
 
