@@ -96,7 +96,10 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is the same in all its lanes: say so, so that what derives
+  // from it (block counts, buffer resources) stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b0 = part * partition_blocks;
   const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
 
@@ -151,16 +154,28 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     return (int64_t)__builtin_amdgcn_readlane(my_bid, k) * block_stride + head_off;
   };
 
+  // Tile k of this wave as a buffer resource; past the wave's blocks an empty
+  // one (the loads below are issued unconditionally and read nothing then).
+  constexpr uint32_t kTileBytes = 16 * D * 2;
+  auto k_tile = [&](int kk) {
+    const bool valid = kk < nbw;
+    return tile_rsrc(k_pool + tile_off(valid ? kk : 0), valid ? kTileBytes : 0u);
+  };
+  auto v_tile = [&](int kk) {
+    const bool valid = kk < nbw;
+    return tile_rsrc(v_pool + tile_off(valid ? kk : 0), valid ? kTileBytes : 0u);
+  };
+
   KVRegs<D> A, B;
-  if (nbw > 0) {
+  if constexpr (kEarlyRefill) {
+    load_k<D>(A, k_tile(0), lane);
+    load_v<D>(A, v_tile(0), lane);
+    load_k<D>(B, k_tile(1), lane);
+    load_v<D>(B, v_tile(1), lane);
+  } else if (nbw > 0) {
     const int64_t o = tile_off(0);
     load_k<D>(A, k_pool + o, lane);
     load_v<D>(A, v_pool + o, lane);
-  }
-  if (kEarlyRefill && nbw > 1) {
-    const int64_t o = tile_off(1);
-    load_k<D>(B, k_pool + o, lane);
-    load_v<D>(B, v_pool + o, lane);
   }
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
@@ -193,29 +208,41 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   WaveState<D, G> st;
   wave_init(st);
 
-  // Blocks k (in A) and k+1 (in B) per trip, buffer roles fixed so both stay
-  // in registers.
   auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
-  for (int k = 0; k < nbw; k += 2) {
-    if constexpr (kEarlyRefill) {
-      // block k+2 goes into A (K after the scores, V after P.V), k+3 into B
-      const int64_t oa = k + 2 < nbw ? tile_off(k + 2) : 0;
+  if constexpr (kEarlyRefill) {
+    // Blocks k (in A) and k+1 (in B) per trip, buffer roles fixed so both
+    // stay in registers; block k+2 goes into A (K after the scores, V after
+    // P.V), k+3 into B, through buffer resources that are empty past the
+    // wave's blocks; an odd last block (in A) after the loop.  The trip has
+    // no branch around a load and no exit in its middle: with either, the
+    // compiler merges buffer registers or sinks loads into one path, and
+    // the wait counts it then assumes at the top of the loop drain the
+    // prefetch.
+    int k = 0;
+    for (; k + 1 < nbw; k += 2) {
+      const auto ka = k_tile(k + 2), va = v_tile(k + 2);
+      const auto kb = k_tile(k + 3), vb = v_tile(k + 3);
       block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 2 < nbw) load_k<D>(A, k_pool + oa, lane);
+      load_k<D>(A, ka, lane);
       block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 2 < nbw) load_v<D>(A, v_pool + oa, lane);
-      if (k + 1 >= nbw) break;
-      const int64_t ob = k + 3 < nbw ? tile_off(k + 3) : 0;
+      load_v<D>(A, va, lane);
       block_scores<D, G>(B, s_q, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], knew, lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 3 < nbw) load_k<D>(B, k_pool + ob, lane);
+      load_k<D>(B, kb, lane);
       block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave], vnew, lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (k + 3 < nbw) load_v<D>(B, v_pool + ob, lane);
-    } else {
-      // block k+1 goes into B before A is computed, k+2 into A before B
+      load_v<D>(B, vb, lane);
+    }
+    if (k < nbw) {
+      block_scores<D, G>(A, s_q, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
+      block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
+    }
+  } else {
+    // d = 256 (one block is 16 KiB): block k+1 goes into B before A is
+    // computed, k+2 into A before B.
+    for (int k = 0; k < nbw; k += 2) {
       if (k + 1 < nbw) {
         const int64_t o = tile_off(k + 1);
         load_k<D>(B, k_pool + o, lane);

@@ -98,6 +98,36 @@ __device__ __forceinline__ void load_v(KVRegs<D>& r, const uint16_t* __restrict_
     r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
 }
 
+// The same loads through a raw buffer resource over one tile (4 KiB at
+// d = 128): a resource of 0 bytes reads nothing and gives zeros, so a loop
+// can issue its prefetch every trip without a branch (a load under a branch
+// makes the compiler merge the buffer registers at the join, which waits for
+// the load right after issuing it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* tile, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(tile), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ void load_k(KVRegs<D>& r, __amdgpu_buffer_rsrc_t ktile, int lane) {
+  const int base = ((lane & 15) * D + 8 * (lane >> 4)) * 2;
+#pragma unroll
+  for (int c = 0; c < KVRegs<D>::KC; ++c)
+    r.k[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ktile, base + 64 * c, 0, 0));
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(KVRegs<D>& r, __amdgpu_buffer_rsrc_t vtile, int lane) {
+  const int base = (D / 64) * lane * 2;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    if constexpr (D == 128)
+      r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(vtile, base + t * D * 2, 0, 0);
+    else
+      r.v[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vtile, base + t * D * 2, 0, 0));
+  }
+}
+
 // P.V over one token pair for one packed dword of V per token:
 // lo element pair (a.lo, b.lo), hi element pair (a.hi, b.hi).
 template <int G>
