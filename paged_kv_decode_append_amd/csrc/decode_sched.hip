@@ -236,7 +236,10 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
   __shared__ int32_t s_fstart[kMaxSegs + 1];   // first staged block of each segment
   __shared__ int32_t s_bid[kMaxWgBlocks];      // raw block ids of the work-group's blocks
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is the same in all its lanes: say so, so that what derives
+  // from it (block counts, buffer resources) stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
   const int32_t* rec = sched + sched_rec_offset(U) + (int64_t)w * kRecWords;
   // the whole 80-byte record at once (16-byte aligned): head + 4 descriptors
@@ -268,6 +271,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
   auto seg_from_record = [&](int k) -> SegInfo {
     return checked(reinterpret_cast<const int4*>(
         sched + sched_ovf_offset(U, nwg) + 4 * (int64_t)(ob + k - kInlineSegs))[0]);
+  };
+  // a segment descriptor read from LDS, as scalars (the same for every lane)
+  auto seg_at = [&](int k) -> SegInfo {
+    const SegInfo sg = s_seg[k];
+    return SegInfo{__builtin_amdgcn_readfirstlane(sg.u), __builtin_amdgcn_readfirstlane(sg.jb),
+                   __builtin_amdgcn_readfirstlane(sg.je), __builtin_amdgcn_readfirstlane(sg.ctx)};
   };
   auto nbw_of = [&](const SegInfo& sg) {
     return max(0, (sg.je - sg.jb - wave + kWaves - 1) / kWaves);
@@ -434,11 +443,21 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     return;  // as above (uniform)
   }
 
-  // Pool offset of this wave's k-th block of segment s.
+  // Pool offset of this wave's k-th block of segment s (a scalar).
   auto tile_off = [&](int s, int k) -> int64_t {
-    const int g = s_seg[s].u % num_kv_heads;
-    const int32_t f = s_fstart[s] + wave + kWaves * k;
-    return clamp_bid(s_bid[f]) * block_stride + (int64_t)g * tile_elems;
+    const int g = __builtin_amdgcn_readfirstlane(s_seg[s].u % num_kv_heads);
+    const int32_t f = __builtin_amdgcn_readfirstlane(s_fstart[s]) + wave + kWaves * k;
+    return clamp_bid(__builtin_amdgcn_readfirstlane(s_bid[f])) * block_stride +
+           (int64_t)g * tile_elems;
+  };
+  // Tile (cs, kk) as buffer resources; empty when the cursor has no block
+  // there (the loads are issued unconditionally and read nothing then).
+  constexpr uint32_t kTileBytes = 16 * D * 2;
+  auto k_rsrc = [&](bool valid, int64_t o) {
+    return tile_rsrc(k_pool + (valid ? o : 0), valid ? kTileBytes : 0u);
+  };
+  auto v_rsrc = [&](bool valid, int64_t o) {
+    return tile_rsrc(v_pool + (valid ? o : 0), valid ? kTileBytes : 0u);
   };
   // Refill cursor: the stream pair (cs, ck), (cs, ck + 1) that A and B load
   // next (ck even; every segment has an even number of positions).
@@ -447,7 +466,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     while (cs < nseg && ck >= ((cn + 1) & ~1)) {
       ck -= (cn + 1) & ~1;
       ++cs;
-      cn = cs < nseg ? nbw_of(s_seg[cs]) : 0;
+      cn = cs < nseg ? nbw_of(seg_at(cs)) : 0;
     }
   };
   auto cursor_advance = [&]() {
@@ -458,22 +477,24 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
   // starts with the next segment's first pair.
   if (n0 == 0) {
     cursor_skip();
-    if (cs < nseg && ck < cn) {
+    if constexpr (kEarlyRefill) {
+      const bool ra = cs < nseg && ck < cn, rb = cs < nseg && ck + 1 < cn;
+      const int64_t oa = ra ? tile_off(cs, ck) : 0, obb = rb ? tile_off(cs, ck + 1) : 0;
+      load_k<D>(A, k_rsrc(ra, oa), lane);
+      load_v<D>(A, v_rsrc(ra, oa), lane);
+      load_k<D>(B, k_rsrc(rb, obb), lane);
+      load_v<D>(B, v_rsrc(rb, obb), lane);
+    } else if (cs < nseg && ck < cn) {
       const int64_t o = tile_off(cs, ck);
       load_k<D>(A, k_pool + o, lane);
       load_v<D>(A, v_pool + o, lane);
-    }
-    if (kEarlyRefill && cs < nseg && ck + 1 < cn) {
-      const int64_t o = tile_off(cs, ck + 1);
-      load_k<D>(B, k_pool + o, lane);
-      load_v<D>(B, v_pool + o, lane);
     }
   }
   cursor_advance();  // the cursor now points at the pair after the first one
 
   WaveState<D, G> st;
   for (int s = 0; s < nseg; ++s) {
-    const SegInfo sg = s_seg[s];
+    const SegInfo sg = seg_at(s);
     const int i = sg.u / num_kv_heads, g = sg.u - i * num_kv_heads;
     const int ctx = sg.ctx;
     const int nblk_u = (ctx + 15) >> 4;
@@ -488,44 +509,66 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     uint4 qnext[QPT];
     NewRows rnext{uint4{0u, 0u, 0u, 0u}, uint4{0u, 0u, 0u, 0u}, 0};
     if (s + 1 < nseg) {
-      fetch_q(s_seg[s + 1], qnext);
-      rnext = fetch_new(s_seg[s + 1]);
+      const SegInfo sn = seg_at(s + 1);
+      fetch_q(sn, qnext);
+      rnext = fetch_new(sn);
     }
 
     wave_init(st);
     const int nbw = nbw_of(sg);
     auto tok_of = [&](int kk) { return (sg.jb + wave + kWaves * kk) * 16; };
-    for (int k = 0; k < nbw; k += 2) {
-      // block k of this segment is in A, k + 1 in B; the cursor names the
-      // pair they are refilled with (possibly in a following segment)
-      const bool ra = cs < nseg && ck < cn;
-      const bool rb = cs < nseg && ck + 1 < cn;
-      const int64_t oa = ra ? tile_off(cs, ck) : 0;
-      const int64_t obb = rb ? tile_off(cs, ck + 1) : 0;
-      cursor_advance();
-      if constexpr (kEarlyRefill) {
-        // A: K after the scores, V after P.V; then B likewise
+    if constexpr (kEarlyRefill) {
+      // Block k of this segment is in A, k + 1 in B; the cursor names the
+      // pair they are refilled with (possibly in a following segment),
+      // through buffer resources that are empty where it has no block.  No
+      // branch around a load and no exit in the middle of a trip (either
+      // makes the compiler drain the prefetch at the top of the loop); an
+      // odd last block after the loop, with B refilled there.
+      int k = 0;
+      for (; k + 1 < nbw; k += 2) {
+        const bool ra = cs < nseg && ck < cn;
+        const bool rb = cs < nseg && ck + 1 < cn;
+        const int64_t oa = ra ? tile_off(cs, ck) : 0;
+        const int64_t obb = rb ? tile_off(cs, ck + 1) : 0;
+        cursor_advance();
+        const auto ka = k_rsrc(ra, oa), va = v_rsrc(ra, oa);
+        const auto kb = k_rsrc(rb, obb), vb = v_rsrc(rb, obb);
         block_scores<D, G>(A, qs, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (ra) load_k<D>(A, k_pool + oa, lane);
+        load_k<D>(A, ka, lane);
         block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (ra) load_v<D>(A, v_pool + oa, lane);
-        if (k + 1 >= nbw) {
-          // odd count: position k + 1 is this segment's empty slot
-          if (rb) {
-            load_k<D>(B, k_pool + obb, lane);
-            load_v<D>(B, v_pool + obb, lane);
-          }
-          break;
-        }
+        load_v<D>(A, va, lane);
         block_scores<D, G>(B, qs, st, tok_of(k + 1), ctx, scale_log2, s_p[wave], knew, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (rb) load_k<D>(B, k_pool + obb, lane);
+        load_k<D>(B, kb, lane);
         block_pv<D, G>(B, st, tok_of(k + 1), ctx, s_p[wave], vnew, lane);
         __builtin_amdgcn_sched_barrier(0);
-        if (rb) load_v<D>(B, v_pool + obb, lane);
-      } else {
+        load_v<D>(B, vb, lane);
+      }
+      if (k < nbw) {
+        // odd count: position k + 1 is this segment's empty slot
+        const bool ra = cs < nseg && ck < cn;
+        const bool rb = cs < nseg && ck + 1 < cn;
+        const int64_t oa = ra ? tile_off(cs, ck) : 0;
+        const int64_t obb = rb ? tile_off(cs, ck + 1) : 0;
+        cursor_advance();
+        const auto ka = k_rsrc(ra, oa), va = v_rsrc(ra, oa);
+        const auto kb = k_rsrc(rb, obb), vb = v_rsrc(rb, obb);
+        block_scores<D, G>(A, qs, st, tok_of(k), ctx, scale_log2, s_p[wave], knew, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_k<D>(A, ka, lane);
+        block_pv<D, G>(A, st, tok_of(k), ctx, s_p[wave], vnew, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_v<D>(A, va, lane);
+        load_k<D>(B, kb, lane);
+        load_v<D>(B, vb, lane);
+      }
+    } else {
+      for (int k = 0; k < nbw; k += 2) {
+        const bool ra = cs < nseg && ck < cn;
+        const int64_t oa = ra ? tile_off(cs, ck) : 0;
+        cursor_advance();
         // B takes block k + 1 (this pair) before A is computed; A takes the
         // cursor's first position before B is computed
         if (k + 1 < nbw) {
