@@ -192,6 +192,39 @@ __device__ __forceinline__ void load8(KV8Regs<D>& r, const uint8_t* __restrict__
   }
 }
 
+// The same block through raw buffer resources (codes of K and V, 16 row
+// scales each); resources of 0 bytes read nothing and give zeros, so the
+// loop issues its prefetch unconditionally, without a branch or a re-read.
+struct Block8Rsrc {
+  __amdgpu_buffer_rsrc_t k, v, ks, vs;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc8(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ void load8(KV8Regs<D>& r, const Block8Rsrc& t, int lane) {
+  const int row = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2)
+    r.k[c2] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(t.k, row * D + 64 * c2 + 16 * grp, 0, 0));
+  r.ks = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(t.ks, 16 * grp, 0, 0));
+  r.vs = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(t.vs, 16 * grp, 0, 0));
+  if constexpr (V8Layout<D>::HALF) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          t.v, (8 * (lane >> 5) + j) * D + 4 * (lane & 31), 0, 0);
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt)
+      r.v[tt] = __builtin_amdgcn_raw_buffer_load_b32(t.v, tt * D + 4 * lane, 0, 0);
+  }
+}
+
 template <int D, int G>
 __device__ __forceinline__ void wave8_init(Wave8<D, G>& st) {
   st.m = -__builtin_huge_valf();
@@ -376,9 +409,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
   constexpr int EPL = D / 64;
   constexpr int GP = (G + 3) & ~3;
-  // blocks in flight per wave: 16 KiB at d = 128 and at d = 256 up to G = 5
-  // (larger groups keep one block, to stay within 256 registers)
-  constexpr int NBUF = D == 128 ? 4 : (G <= 5 ? 2 : 1);
+  // blocks in flight per wave (4 KiB each at d = 128, 8 KiB at d = 256),
+  // as many as fit in 256 registers without spilling
+  constexpr int NBUF = D == 128 ? (G <= 2 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 2 : 1);
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
@@ -390,7 +423,9 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is the same in all its lanes (kept in scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b0 = part * partition_blocks;
   const int32_t* bt_row = block_tables + (int64_t)i * max_blocks_per_seq;
 
@@ -423,15 +458,18 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   const int64_t tile = (int64_t)16 * D;           // bytes of one block of one head
   const int64_t head_off = (int64_t)g * tile;
   const int64_t block_stride = (int64_t)num_kv_heads * tile;
-  // Loads are issued unconditionally (a block index past the wave's last one
-  // re-reads that block, an L2 hit, and is never used): a load under a branch
-  // makes the compiler copy the buffer at the join and wait for all loads.
-  const int last = max(nbw - 1, 0);
+  // Loads are issued unconditionally, through buffer resources that are
+  // empty past the wave's last block: a load under a branch makes the
+  // compiler merge the buffer registers at the join and wait for all loads.
   auto load_block = [&](KV8Regs<D>& r, int k) {
-    const int64_t bid = __builtin_amdgcn_readlane(my_bid, min(k, last));
+    const bool valid = k < nbw;
+    const int64_t bid = __builtin_amdgcn_readlane(my_bid, valid ? k : 0);
     const int64_t o = bid * block_stride + head_off;
     const int64_t so = (bid * num_kv_heads + g) * 16;
-    load8<D>(r, k_codes + o, v_codes + o, k_scale + so, v_scale + so, lane);
+    const uint32_t cb = valid ? (uint32_t)tile : 0u, sb = valid ? 64u : 0u;
+    const Block8Rsrc t{rsrc8(k_codes + o, cb), rsrc8(v_codes + o, cb), rsrc8(k_scale + so, sb),
+                       rsrc8(v_scale + so, sb)};
+    load8<D>(r, t, lane);
   };
 
   KV8Regs<D> buf[NBUF];
@@ -475,14 +513,25 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   Wave8<D, G> st;
   wave8_init(st);
   auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
-  for (int k = 0; k < nbw; k += NBUF) {
+  // NBUF blocks per trip with no exit in its middle (with one, the compiler
+  // sinks loads into the continuing path and the wait counts at the top of
+  // the loop drain the prefetch); the last nbw % NBUF blocks after it.
+  int k = 0;
+  for (; k + NBUF <= nbw; k += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
-      if (k + j >= nbw) break;
       const float vmax = block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2,
                                              s_p[wave], knew, ksnew, vsnew, lane);
       block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, vnew, lane);
       load_block(buf[j], k + j + NBUF);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j + 1 < NBUF; ++j) {
+    if (k + j < nbw) {
+      const float vmax = block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2,
+                                             s_p[wave], knew, ksnew, vsnew, lane);
+      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, vnew, lane);
     }
   }
 
