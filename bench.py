@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="capture the whole step (all layers) once as a HIP graph and time "
                          "its replays")
+    ap.add_argument("--one-call", action="store_true",
+                    help="every layer of a step in one library call "
+                         "(pkv_append_attention_layers) instead of one call per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-dtype", choices=["fp16", "fp8"], default="fp16",
                     help="cache element type: fp16 (the workloads' own), or fp8 E4M3 codes "
@@ -275,6 +278,12 @@ def main():
         for c, t, o in zip(caches, layers, outs):
             step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=fused)
 
+    if args.one_call:
+        if not fused or args.graph:
+            print(json.dumps({"error": "--one-call is the fused eager step; drop --separate/--graph"}))
+            sys.exit(2)
+        run_step = step.prepare_layers([(c, t["q"], t["k_new"], t["v_new"], o)
+                                        for c, t, o in zip(caches, layers, outs)])
     if args.graph:
         run_step()
         graph = step.capture([(c, t["q"], t["k_new"], t["v_new"], o)
@@ -313,7 +322,9 @@ def main():
             for c, t in zip(caches, layers):
                 pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
         ev[r][0].record(stream)
-        for c, t, o in zip(caches, layers, outs):
+        if args.one_call:
+            run_step.attend()
+        for c, t, o in zip(caches, layers, outs) if not args.one_call else ():
             if fused:
                 step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=True)
             else:
@@ -375,7 +386,9 @@ def main():
                        else "quantizing, fused into the decode kernel") if fused
                       else "separate kernel",
             "kv_cache": "fp16" if args.kv_dtype == "fp16" else "fp8_e4m3 + fp32 row scales",
-            "launch": "one HIP graph per step" if args.graph else "one library call per layer",
+            "launch": ("one HIP graph per step" if args.graph else
+                       "one library call per step" if args.one_call else
+                       "one library call per layer"),
         },
         "roofline": {
             "bound": "hbm",

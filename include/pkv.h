@@ -323,6 +323,41 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
                               void* stream);
 
 /*
+ * pkv_append_attention_step for every layer of one step, in one call: for
+ * l = 0 .. num_layers-1, in that order on `stream`, exactly
+ *   pkv_append_attention_step(&caches[l], k_new[l], v_new[l], slot_mapping,
+ *       num_tokens, q[l], out[l], block_tables, ...)
+ * with the arguments after out[l] shared by all layers (block tables,
+ * context lengths and slots are per step; the pools, new rows, queries and
+ * outputs are per layer).  A step issues two to four small launches per
+ * layer and the host cost of a layer's call is paid once per launch
+ * (danielfleming.xyz, "Static batching", section "What changed": the kernel
+ * launches of a pass cost more host time than the GPU spends); this entry
+ * point leaves one call per step.
+ *
+ *   caches                  host array [num_layers] of cache descriptors
+ *   k_new, v_new, q, out    host arrays [num_layers] of device pointers
+ *   num_layers              >= 0 (0: nothing is launched)
+ *   other arguments         as for pkv_append_attention_step; the one
+ *                           workspace serves every layer (stream order).
+ * Every argument is checked before the first launch (all layers'
+ * descriptors included); the first launch error stops the loop and is
+ * returned (the layers before it are enqueued).
+ * Errors: as for pkv_append_attention_step.
+ */
+int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,
+                                const void* const* k_new, const void* const* v_new,
+                                const int64_t* slot_mapping, int32_t num_tokens,
+                                const void* const* q, void* const* out,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_heads,
+                                float scale, int32_t max_context_len, int32_t max_query_len,
+                                int32_t kv_partition_tokens, const void* schedule,
+                                size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * Debug validator (host, synchronous, no GPU): checks on host copies of
  * the step's index arrays every device-content contract the hot path
  * assumes.  Returns PKV_OK, or PKV_ERR_CONTRACT with *bad_what set to one

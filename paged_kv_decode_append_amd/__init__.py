@@ -32,7 +32,8 @@ PKV_ERR_CONTRACT = -5
 EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_hip_error", "pkv_slot_mapping", "pkv_kv_append",
     "pkv_attention_workspace_size", "pkv_decode_schedule_size", "pkv_decode_schedule",
-    "pkv_paged_attention_step", "pkv_append_attention_step", "pkv_validate_step",
+    "pkv_paged_attention_step", "pkv_append_attention_step", "pkv_append_attention_layers",
+    "pkv_validate_step",
 )
 
 
@@ -86,6 +87,9 @@ def _load():
     lib.pkv_append_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, P, i32,
                                               P, P, i32, i32, i32, ctypes.c_float, i32, i32, i32,
                                               P, sz, P, sz, P]
+    lib.pkv_append_attention_layers.argtypes = [ctypes.POINTER(_Cache), i32, P, P, P, i32, P, P,
+                                                P, i32, P, P, i32, i32, i32, ctypes.c_float, i32,
+                                                i32, i32, P, sz, P, sz, P]
     lib.pkv_validate_step.argtypes = [P, i32, P, P, i32, i32, i64, i32, P, i32, i32, i32,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     for name in EXPORTED:
@@ -330,6 +334,49 @@ def append_attention_step(cache: KVCache, k_new, v_new, slot_mapping_t, q, out, 
         *_schedule_args(schedule), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_append_attention_step")
     return out
+
+
+class AttentionLayers:
+    """Every layer of a step in one call (pkv_append_attention_layers).
+
+    Built once from the per-layer caches and tensors, which must stay
+    allocated (their addresses are kept); calling it enqueues
+    pkv_append_attention_step for each layer in order with the step's shared
+    arguments, in one call into the library."""
+
+    def __init__(self, caches, k_new, v_new, q, out):
+        import torch
+        L = len(caches)
+        if not (len(k_new) == len(v_new) == len(q) == len(out) == L):
+            raise ValueError("one cache, k_new, v_new, q and out per layer")
+        for i in range(L):
+            for t, name in ((k_new[i], "k_new"), (v_new[i], "v_new"), (q[i], "q"), (out[i], "out")):
+                _need(t, torch.float16, name)
+            if v_new[i].shape != k_new[i].shape or q[i].shape != q[0].shape or \
+                    out[i].shape != q[0].shape or k_new[i].shape != k_new[0].shape:
+                raise ValueError("every layer's tensors must have the same shapes")
+        self.num_layers = L
+        self.num_tokens = int(k_new[0].shape[0]) if L else 0
+        self.num_q_heads = int(q[0].shape[1]) if L else 0
+        self._keep = (list(caches), list(k_new), list(v_new), list(q), list(out))
+        self._caches = (_Cache * max(L, 1))(*[c._c for c in caches])
+        vp = ctypes.c_void_p
+        self._k = (vp * max(L, 1))(*[t.data_ptr() for t in k_new])
+        self._v = (vp * max(L, 1))(*[t.data_ptr() for t in v_new])
+        self._q = (vp * max(L, 1))(*[t.data_ptr() for t in q])
+        self._o = (vp * max(L, 1))(*[t.data_ptr() for t in out])
+
+    def __call__(self, slot_mapping_t, block_tables, context_lens, query_start_loc,
+                 num_decode_seqs: int, scale: float, max_context_len: int, max_query_len: int,
+                 workspace=None, kv_partition_tokens: int = 0, stream=None, schedule=None):
+        rc = lib.pkv_append_attention_layers(
+            self._caches, self.num_layers, self._k, self._v, _ptr(slot_mapping_t),
+            self.num_tokens, self._q, self._o, _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), _ptr(query_start_loc), context_lens.shape[0], num_decode_seqs,
+            self.num_q_heads, float(scale), int(max_context_len), int(max_query_len),
+            int(kv_partition_tokens), *_schedule_args(schedule), _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _stream(stream))
+        _check(rc, "pkv_append_attention_layers")
 
 
 def validate_step(block_tables, context_lens, query_start_loc, num_decode_seqs: int,

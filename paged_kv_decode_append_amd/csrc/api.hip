@@ -329,6 +329,42 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
                         workspace_bytes, stream);
 }
 
+int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,
+                                const void* const* k_new, const void* const* v_new,
+                                const int64_t* slot_mapping, int32_t num_tokens,
+                                const void* const* q, void* const* out,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_heads,
+                                float scale, int32_t max_context_len, int32_t max_query_len,
+                                int32_t kv_partition_tokens, const void* schedule,
+                                size_t schedule_bytes, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (num_layers < 0) return PKV_ERR_INVALID_ARG;
+  if (num_layers == 0) return PKV_OK;
+  if (!caches || !k_new || !v_new || !q || !out) return PKV_ERR_INVALID_ARG;
+  // every layer's descriptor and pointers before the first launch
+  for (int32_t l = 0; l < num_layers; ++l) {
+    int rc = check_cache(&caches[l]);
+    if (rc != PKV_OK) return rc;
+    rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, caches[l].num_kv_heads,
+                          caches[l].head_dim, max_context_len, max_query_len,
+                          kv_partition_tokens);
+    if (rc != PKV_OK) return rc;
+    if (!k_new[l] || !v_new[l] || (num_seqs > 0 && (!q[l] || !out[l])))
+      return PKV_ERR_INVALID_ARG;
+  }
+  for (int32_t l = 0; l < num_layers; ++l) {
+    const int rc = attention_step(&caches[l], k_new[l], v_new[l], slot_mapping, num_tokens, q[l],
+                                  out[l], block_tables, max_blocks_per_seq, context_lens,
+                                  query_start_loc, num_seqs, num_decode_seqs, num_q_heads, scale,
+                                  max_context_len, max_query_len, kv_partition_tokens, schedule,
+                                  schedule_bytes, workspace, workspace_bytes, stream);
+    if (rc != PKV_OK) return rc;
+  }
+  return PKV_OK;
+}
+
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, const int32_t* query_start_loc,
                       int32_t num_seqs, int32_t num_decode_seqs, int64_t num_blocks,

@@ -35,8 +35,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (KVCache, append_attention_step, attention_workspace_size, decode_schedule,
-               decode_schedule_size, kv_append, paged_attention_step, slot_mapping)
+from . import (AttentionLayers, KVCache, append_attention_step, attention_workspace_size,
+               decode_schedule, decode_schedule_size, kv_append, paged_attention_step,
+               slot_mapping)
 
 
 class Step:
@@ -108,6 +109,28 @@ class Step:
                 self.layer(cache, q, k_new, v_new, out, fused=fused)
         torch.cuda.current_stream().wait_stream(side)
         return graph
+
+    def prepare_layers(self, layers):
+        """One library call per step for all layers (pkv_append_attention_layers).
+
+        layers: per layer (cache, q, k_new, v_new, out), tensors that stay
+        allocated.  Returns run(stream=None): plan() then every layer's
+        append + attention, as plan() followed by layer(..., fused=True) per
+        layer."""
+        caches, qs, ks, vs, outs = (list(x) for x in zip(*layers))
+        batch = AttentionLayers(caches, ks, vs, qs, outs)
+
+        def attend(stream=None):
+            batch(self.slot_mapping, self.block_tables, self.context_lens, self.query_start_loc,
+                  self.num_decode_seqs, self.scale, self.max_context_len, self.max_query_len,
+                  workspace=self.workspace, kv_partition_tokens=self.kv_partition_tokens,
+                  stream=stream, schedule=self.schedule)
+
+        def run(stream=None):
+            self.plan(stream=stream)
+            attend(stream)
+        run.attend = attend  # the layers' call alone (plan() already done)
+        return run
 
     def layer(self, cache: KVCache, q, k_new, v_new, out, stream=None, fused: bool = True):
         """Append this layer's new K/V, then attend (one call when fused)."""

@@ -118,6 +118,33 @@ def test_fused_step_argument_errors():
     assert _fused(c, nseq=0, ndec=0, T=0) == pkv.PKV_OK
 
 
+def _layers(caches, L=None, kn=FAKE, vn=FAKE, q=FAKE, out=FAKE, T=4, nseq=4, ndec=4, hq=12,
+            mcl=1024, maxblk=64):
+    L = len(caches) if L is None else L
+    arr = (pkv._Cache * max(len(caches), 1))(*caches)
+    ptrs = lambda p: None if p is None else (ctypes.c_void_p * max(len(caches), 1))(*([p] * len(caches)))
+    return pkv.lib.pkv_append_attention_layers(arr, L, ptrs(kn), ptrs(vn), FAKE, T, ptrs(q),
+                                               ptrs(out), FAKE, maxblk, FAKE, None, nseq, ndec,
+                                               hq, 0.1, mcl, 1, 0, None, 0, None, 0, None)
+
+
+def test_layers_argument_errors_are_found_before_any_launch():
+    """Every layer is checked before the first launch: a bad descriptor or a
+    missing pointer in the last layer fails the call with nothing enqueued
+    (no GPU here: a launch would fail with PKV_ERR_HIP instead)."""
+    good = _cache()
+    assert _layers([good, good], L=-1) == -1
+    assert _layers([good, good], L=0) == pkv.PKV_OK
+    assert _layers([good, _cache(head_dim=64)]) == -2
+    assert _layers([good, good], kn=None) == -1
+    assert _layers([good, good], out=None) == -1
+    assert _layers([good, good], hq=18) == -2
+    assert _layers([good, good], nseq=0, ndec=0, T=0) == pkv.PKV_OK   # empty step
+    assert pkv.lib.pkv_append_attention_layers(None, 2, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 64,
+                                               FAKE, None, 4, 4, 12, 0.1, 1024, 1, 0, None, 0,
+                                               None, 0, None) == -1
+
+
 def test_decode_schedule_size_and_argument_errors():
     # d = 128 steps get a schedule; d = 256 keeps the partition grid
     assert pkv.decode_schedule_size(83, 2, 128, 4352) > 0
