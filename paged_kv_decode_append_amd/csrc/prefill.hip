@@ -318,9 +318,10 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     }
   };
 
-  // fp8: O is kept in units of vref, the largest V row scale seen so far (a
-  // power of two; O is rescaled when a tile brings a larger one), so that
-  // every fp16 weight p 2^(e_t) / vref stays <= p
+  // fp8: O is kept in units of vref, the largest V row scale of the current
+  // tile (a power of two; O is rescaled, exactly, when the next tile's
+  // differs), so that every fp16 weight p 2^(e_t) / vref stays <= p and
+  // loses range only against the rows of its own tile
   float vref = 0.f, inv_vref = 0.f;
   TileRegs<FP8> next;
   if (kt_begin < kt_end) load_tile(next, kt_begin);
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
       // lanes of one lgrp hold the same tokens; the four groups cover the tile
       vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
       vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
-      if (vmax > vref) {  // the same in every lane and wave
+      if (vmax != vref) {  // the same in every lane and wave
         const float ratio = vref / vmax;  // exact: powers of two (0 before the first tile)
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)

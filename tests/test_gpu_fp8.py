@@ -73,8 +73,9 @@ def test_append_quantizes_every_fp16_value_bit_exactly(d):
     assert np.array_equal(_np(dev["vs"]).view(np.uint32), vs.view(np.uint32)), "V scales"
 
 
-def _fp8_cache(wl, layer=0, poison=True):
-    t = workloads.layer_tensors_fp8(wl, layer, device="cuda")
+def _fp8_cache(wl, layer=0, poison=True, scale_exp=(-6, -2), v_scale_exp=None):
+    t = workloads.layer_tensors_fp8(wl, layer, device="cuda", scale_exp=scale_exp,
+                                    v_scale_exp=v_scale_exp)
     if poison:
         # stale rows (outside every context) hold NaN codes and NaN scales
         qsl = np.concatenate([[0], np.cumsum(wl.context_lens)]).astype(np.int32)
@@ -244,6 +245,43 @@ def test_qwen_mixed_full_size_fp8():
                                          wl.scale)
     e2 = assert_close(got[r0 + rows], sub_ref, "qwen_mixed fp8 chunk rows")
     _report("qwen_mixed fp8 layer 5", (max(errs[0], e2[0]), max(errs[1], e2[1])))
+
+
+@pytest.mark.parametrize("kind", ["decode", "short", "long"])
+def test_row_scales_spanning_a_wide_range(kind):
+    """K row scales from 2^-11 to 2^7 move the logits over many orders of
+    magnitude (saturated softmax rows included); V row scales from 2^-4 to
+    2^3 make the per-block (decode) and per-tile (prefill) reference scale
+    change from block to block.  The V range is kept to 2^8: the weights are
+    fp16, so the error of an output element scales with sum_t w_t |v_t|, and
+    a much wider V range makes rows whose output is a small difference of
+    large terms (relative error grows with that ratio, in any fp16-weight
+    kernel).  The result stays within the tolerance of the oracle over the
+    exactly dequantized cache."""
+    if kind == "decode":
+        ctx, new, ndec = [1, 16, 17, 300, 1025, 2500], [1] * 6, 6
+    else:
+        ctx, new, ndec = FP8_CHUNKS[kind]
+    wl = workloads.custom(f"fp8_wide_{kind}", ctx, new, ndec, 12, 2, 128, seed=53)
+    t = _fp8_cache(wl, scale_exp=(-11, 8), v_scale_exp=(-4, 4))
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, fused=True)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    # The 2e-3 bound is stated for unit-scale values; here rows reach ~10^3
+    # and fp16 output rounding alone is 2^-11 of the value, so the
+    # elementwise bound is taken relative to each row's largest |value|
+    # (at least 1); the norm-relative bound is unchanged.
+    r = ref.reshape(-1, ref.shape[-1])
+    d = np.abs(got.reshape(r.shape) - r)
+    row_scale = np.maximum(1.0, np.abs(r).max(axis=1))
+    scaled = float((d.max(axis=1) / row_scale).max())
+    norm_rel = float((np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)).max())
+    assert scaled <= 2e-3 and norm_rel <= 1e-2, f"scaled max_abs={scaled:.2e} norm_rel={norm_rel:.2e}"
+    _report(f"fp8 wide scales {kind} (row-scaled)", (scaled, norm_rel))
 
 
 @pytest.mark.parametrize("name", ["qwen_uniform", "qwen_ragged", "qwen_spec"])

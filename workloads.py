@@ -220,13 +220,16 @@ def custom(name: str, ctx, new, num_decode_seqs: int, hq: int, hkv: int, d: int,
                   pool_blocks=pool_blocks)
 
 
-def layer_tensors_fp8(wl: Workload, layer: int, device="cpu"):
+def layer_tensors_fp8(wl: Workload, layer: int, device="cpu", scale_exp=(-6, -2),
+                      v_scale_exp=None):
     """An fp8 (E4M3) cache of one layer with N(0,1)-like values, drawn
     directly as bytes: k_codes, v_codes uint8 [NB, Hkv, 16, d] with random
     sign, exponent field 4..10 and mantissa (values 2^-3 .. ~15, no NaN
     codes), k_scale, v_scale float32 [NB, Hkv, 16] random powers of two
-    2^-6 .. 2^-3; plus fp16 q, k_new, v_new as layer_tensors.  Drawn with a
-    torch generator seeded by (seed, layer) on `device`."""
+    2^lo .. 2^(hi-1) for scale_exp = (lo, hi) (default 2^-6 .. 2^-3; V's
+    from v_scale_exp when given); plus fp16 q, k_new, v_new as
+    layer_tensors.  Drawn with a torch generator seeded by (seed, layer) on
+    `device`."""
     import torch
 
     dev = torch.device(device)
@@ -243,13 +246,15 @@ def layer_tensors_fp8(wl: Workload, layer: int, device="cpu"):
         c |= randint(0, 8, shape, torch.uint8)
         return c
 
-    def scales():
-        return torch.exp2(randint(-6, -2, shape[:3], torch.int32).to(torch.float32))
+    def scales(lo, hi):
+        return torch.exp2(randint(lo, hi, shape[:3], torch.int32).to(torch.float32))
 
     t = layer_tensors(Workload(wl.name, wl.num_layers, wl.num_q_heads, wl.num_kv_heads,
                                wl.head_dim, wl.context_lens, wl.new_tokens, wl.num_decode_seqs,
                                1, wl.block_tables, wl.seed), layer, device)
-    return {"k_codes": codes(), "v_codes": codes(), "k_scale": scales(), "v_scale": scales(),
+    vse = scale_exp if v_scale_exp is None else v_scale_exp
+    return {"k_codes": codes(), "v_codes": codes(), "k_scale": scales(*scale_exp),
+            "v_scale": scales(*vse),
             "q": t["q"], "k_new": t["k_new"], "v_new": t["v_new"]}
 
 
