@@ -355,6 +355,11 @@ class AttentionLayers:
             if v_new[i].shape != k_new[i].shape or q[i].shape != q[0].shape or \
                     out[i].shape != q[0].shape or k_new[i].shape != k_new[0].shape:
                 raise ValueError("every layer's tensors must have the same shapes")
+            c = caches[i]
+            if k_new[i].dim() != 3 or k_new[i].shape[1:] != (c.num_kv_heads, c.head_dim):
+                raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+            if q[i].dim() != 3 or q[i].shape[0] != k_new[i].shape[0] or q[i].shape[2] != c.head_dim:
+                raise ValueError("q and out must be [T, num_q_heads, head_dim]")
         self.num_layers = L
         self.num_tokens = int(k_new[0].shape[0]) if L else 0
         self.num_q_heads = int(q[0].shape[1]) if L else 0
@@ -369,6 +374,8 @@ class AttentionLayers:
     def __call__(self, slot_mapping_t, block_tables, context_lens, query_start_loc,
                  num_decode_seqs: int, scale: float, max_context_len: int, max_query_len: int,
                  workspace=None, kv_partition_tokens: int = 0, stream=None, schedule=None):
+        if slot_mapping_t.numel() < self.num_tokens:
+            raise ValueError("slot_mapping shorter than the token count")
         rc = lib.pkv_append_attention_layers(
             self._caches, self.num_layers, self._k, self._v, _ptr(slot_mapping_t),
             self.num_tokens, self._q, self._o, _ptr(block_tables), block_tables.shape[1],
