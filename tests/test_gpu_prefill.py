@@ -50,3 +50,55 @@ def test_qwen_mixed_full_size():
     _, _, errs = run_layer_and_check(wl, 5, poison=False, seq_subset=[0, 17, 40, 63],
                                      row_samples={chunk_seq: rows})
     _report("qwen_mixed layer 5", errs)
+
+
+def test_fused_chunk_append_matches_separate_calls_with_odd_slots():
+    """A step with chunks, some of whose rows are skipped (slot -1: the
+    pool's current row is attended) and one written to a slot outside its
+    table position (written there, not attended): the fused call gives the
+    same bits as pkv_kv_append followed by pkv_paged_attention_step, in the
+    output and in both pools."""
+    import torch
+    import oracle
+    import paged_kv_decode_append_amd as pkv
+    from paged_kv_decode_append_amd.step import Step
+    from parity import host_bits, poison_stale
+
+    ctx, new = [40, 300, 129, 90], [1, 70, 129, 6]
+    wl = workloads.custom("odd_slots", ctx, new, 1, 12, 2, 128, seed=61, pool_factor=2.0)
+    qsl = wl.query_start_loc
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, 16).copy()
+    used = set(slots.tolist())
+    free = next(s for s in range(wl.num_blocks * 16) if s not in used and s // 16 not in
+                set(wl.block_tables.ravel().tolist()))
+    slots[qsl[1] + 3] = -1                 # long chunk: a padding row
+    slots[qsl[2] + 64] = -1                # second row tile of the 129-row chunk
+    slots[qsl[3] + 5] = -1                 # packed-size chunk, last row
+    slots[qsl[1] + 10] = free              # written elsewhere, not attended
+    outs, pools = [], []
+    for fused in (True, False):
+        t = workloads.layer_tensors(wl, 0, device="cuda")
+        poison_stale(wl, t, poison_new=False)
+        step = Step.from_workload(wl)
+        step.plan()                         # the step's decode schedule (slots given below)
+        sm = torch.from_numpy(slots).cuda()
+        out = torch.full_like(t["q"], float("nan"))
+        cache = pkv.KVCache(t["k_pool"], t["v_pool"])
+        if fused:
+            pkv.append_attention_step(cache, t["k_new"], t["v_new"], sm, t["q"], out,
+                                      step.block_tables, step.context_lens, step.query_start_loc,
+                                      wl.num_decode_seqs, wl.scale, step.max_context_len,
+                                      step.max_query_len, workspace=step.workspace,
+                                      schedule=step.schedule)
+        else:
+            pkv.kv_append(cache, t["k_new"], t["v_new"], sm)
+            pkv.paged_attention_step(cache, t["q"], out, step.block_tables, step.context_lens,
+                                     step.query_start_loc, wl.num_decode_seqs, wl.scale,
+                                     step.max_context_len, step.max_query_len,
+                                     workspace=step.workspace, schedule=step.schedule)
+        torch.cuda.synchronize()
+        outs.append(host_bits(out))
+        pools.append((host_bits(t["k_pool"]), host_bits(t["v_pool"])))
+    assert np.array_equal(outs[0], outs[1]), "output"
+    assert np.array_equal(pools[0][0], pools[1][0]) and np.array_equal(pools[0][1], pools[1][1])
+    assert not np.isnan(outs[0].view(np.float16).astype(np.float32)).any()
