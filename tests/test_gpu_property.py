@@ -1,0 +1,101 @@
+"""Property test: random small steps (hypothesis) on the GPU against the CPU
+oracle.  Each example draws head size, KV heads and query group, a mix of
+single-token decodes and causal chunks (1..160 rows, some covering the whole
+context, others after a cached prefix) with ragged contexts, the split-KV
+partition length, fused or separate append, and an fp16 or fp8 cache.
+Checks, as the fixed-case tests do: slot mapping and pools bit-exact after
+the append, every query row within the attention tolerance.
+
+The search is derandomized (the same examples on every run) and does not
+shrink, so a failure costs one more example, not a search; each example
+prints its case before it runs."""
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, Phase, given, settings, strategies as st
+
+import oracle
+import paged_kv_decode_append_amd as pkv
+import workloads
+from oracle import fp8 as ofp8
+from paged_kv_decode_append_amd.step import Step
+from parity import all_position_slots, assert_close, host_bits, run_layer_and_check
+
+pytestmark = pytest.mark.gpu
+
+# (head_dim, num_kv_heads, group size) with num_q_heads = kv * group <= 32
+HEAD_SHAPES = [(128, 1, 8), (128, 2, 6), (128, 2, 1), (128, 4, 4), (128, 8, 1), (128, 3, 5),
+               (256, 4, 4), (256, 2, 6), (256, 3, 8), (256, 8, 2), (256, 1, 3)]
+
+
+@st.composite
+def steps(draw):
+    d, hkv, g = draw(st.sampled_from(HEAD_SHAPES))
+    n_dec = draw(st.integers(0, 6))
+    n_chunk = draw(st.integers(0 if n_dec else 1, 3))
+    budget = 6000 if d == 128 else 3000         # context tokens the oracle attends in seconds
+    ctx_len = st.integers(1, budget // (n_dec + n_chunk))
+    ctx = [draw(ctx_len) for _ in range(n_dec + n_chunk)]
+    new = [1] * n_dec
+    for c in ctx[n_dec:]:
+        whole = draw(st.booleans())             # a first chunk: no cached prefix
+        n = min(c, 160) if whole else draw(st.integers(1, min(c, 160)))
+        new.append(n)
+        if whole:
+            ctx[len(new) - 1] = n
+    part = draw(st.sampled_from([0, 0, 64, 128, 192, 1024]))
+    fused = draw(st.booleans())
+    fp8 = draw(st.booleans())
+    seed = draw(st.integers(0, 2**20))
+    return d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed
+
+
+def _fp8_step(wl, part, fused):
+    t = workloads.layer_tensors_fp8(wl, 0, device="cuda")
+    # rows outside every context (the new tokens' slots among them) hold NaN
+    # codes and NaN scales: a read of one before its append gives NaN
+    live = np.zeros(wl.num_blocks * 16, bool)
+    live[all_position_slots(wl)] = True
+    qsl = wl.query_start_loc if wl.num_decode_seqs < wl.num_seqs else None
+    live[oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, 16)] = False
+    dead = torch.from_numpy(np.nonzero(~live)[0]).cuda()
+    for n in ("k_codes", "v_codes"):
+        t[n].transpose(1, 2)[dead // 16, dead % 16] = 0x7F
+    for n in ("k_scale", "v_scale"):
+        t[n].transpose(1, 2)[dead // 16, dead % 16] = float("nan")
+    pre = {n: t[n].cpu().numpy() for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    step = Step.from_workload(wl, kv_partition_tokens=part)
+    step.plan()
+    out = torch.full_like(t["q"], float("nan"))
+    step.layer(pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"]), t["q"],
+               t["k_new"], t["v_new"], out, fused=fused)
+    torch.cuda.synchronize()
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, qsl, 16)
+    assert np.array_equal(step.slot_mapping[: wl.num_tokens].cpu().numpy(), slots)
+    kc, vc, ks, vs = ofp8.kv_append(pre["k_codes"], pre["v_codes"], pre["k_scale"],
+                                    pre["v_scale"], host_bits(t["k_new"]), host_bits(t["v_new"]),
+                                    slots)
+    assert np.array_equal(t["k_codes"].cpu().numpy(), kc)
+    assert np.array_equal(t["v_codes"].cpu().numpy(), vc)
+    assert np.array_equal(t["k_scale"].cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(t["v_scale"].cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    return assert_close(out.cpu().numpy(), ref, wl.name)
+
+
+@settings(max_examples=100, deadline=None, derandomize=True, database=None,
+          phases=(Phase.explicit, Phase.generate), print_blob=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(steps())
+def test_random_steps_match_the_oracle(case):
+    d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed = case
+    name = (f"d={d} Hkv={hkv} G={g} ctx={ctx} new={new} decodes={n_dec} part={part} "
+            f"fused={fused} fp8={fp8} seed={seed}")
+    print(f"[property] {name}", flush=True)
+    wl = workloads.custom("property", ctx, new, n_dec, hkv * g, hkv, d, seed=seed)
+    if fp8:
+        errs = _fp8_step(wl, part, fused)
+    else:
+        _, _, errs = run_layer_and_check(wl, kv_partition_tokens=part, fused=fused)
+    print(f"[property]   max_abs={errs[0]:.2e} norm_rel={errs[1]:.2e}", flush=True)
