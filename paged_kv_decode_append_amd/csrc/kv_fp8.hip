@@ -26,18 +26,21 @@
 //     the query fragments are read from LDS in the same column order.  Each
 //     lane ends with the scores of head l % 16 for 4 tokens, times the rows'
 //     K scales.
-//   V: at d = 128 lanes 0-31 take tokens 0-7 of a block and lanes 32-63
-//     tokens 8-15, four columns each (a 4-byte load per token), and the two
-//     halves are added once at the end; at d = 256 every lane owns 4 columns
-//     of all 16 tokens.  Two consecutive tokens' codes of one column are put
-//     side by side with v_perm_b32 and converted together, so P.V is v_dot2
-//     over token pairs.  The row scales 2^e_t enter the weights: each weight
-//     is scaled by 2^(e_t - e_max) (e_max the block's largest, so weights stay
-//     within fp16), the block's P.V sum is formed apart and added times
-//     2^e_max; the softmax denominator sums the unscaled weights.
-// Half the bytes per block let each wave keep four blocks in flight at
-// d = 128 (two at d = 256 for G <= 5), the same bytes in flight as the fp16
-// kernel.
+//   V: P.V is O = P V on the matrix cores too (v_mfma_f32_16x16x16_f16,
+//     heads as rows, one 16-column tile of d per product): the scores'
+//     output layout (head l % 16, tokens 4 (l / 16) .. +3 in lane l) is
+//     already P's A fragment, so the weights never leave registers.  Lane l
+//     loads those four tokens' codes at columns (d / 16)(l % 16) .. +d/16-1
+//     (one 8- or 16-byte load per token); a 4 x 4 byte transpose with
+//     v_perm_b32 gives each column tile's B fragment, converted to fp16
+//     (exact).  The row scales 2^e_t enter the weights: each weight is
+//     scaled by 2^(e_t - e_max) (e_max the block's largest, so weights stay
+//     within fp16), and the O tiles are kept in units of 2^e_max, rescaled
+//     when it changes from one block to the next; the softmax denominator
+//     sums the unscaled weights.
+// On MI355X this kernel is bound by its per-block arithmetic more than by
+// bytes in flight: with P.V as packed dot products (the fp16 kernel's way) it
+// ran 40% slower at B = 256, ctx 512 than with P.V removed altogether.
 #include <algorithm>
 #include <climits>
 
@@ -139,16 +142,19 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
 
 // ---------------------------------------------------------------- decode ---
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// V layout: at d = 128 lanes 0-31 hold tokens 0-7 and lanes 32-63 tokens
-// 8-15 of a block (HALF), 4 columns per lane; at d = 256 4 columns per lane
-// of all 16 tokens.
+// V in the matrix cores' B layout (P.V as O = P V, 16 x 16 x 16 tiles): lane
+// l holds the codes of tokens 4 (l / 16) .. +3 of a block at columns
+// VB (l % 16) .. +VB-1 (VB = d / 16: one 8- or 16-byte load per token).
+// Column tile ct of the product takes byte ct of each of those four chunks,
+// so output column n of tile ct is d = VB n + ct.
 template <int D>
 struct V8Layout {
-  static constexpr bool HALF = D == 128;
-  static constexpr int TOK = HALF ? 8 : 16;  // tokens per lane
+  static constexpr int VB = D / 16;  // codes per token per lane = column tiles
+  static constexpr int VW = VB / 4;  // their 32-bit words
 };
 
 // K in the matrix cores' A layout: lane l holds 16 codes of token row l % 16
@@ -160,37 +166,16 @@ struct KV8Regs {
   uint4 k[K16];
   float4 ks;                          // K scales of tokens 4 (l / 16) .. +3
   float4 vs;                          // their V scales
-  uint32_t v[V8Layout<D>::TOK];       // 4 V codes of each of this lane's tokens
+  uint32_t v[4][V8Layout<D>::VW];     // V codes of those 4 tokens (B layout)
 };
 
 template <int D, int G>
 struct Wave8 {
-  float m;         // running max of this lane's head (lane % 16), base 2
-  float l;         // sum of its weights over this lane's tokens
-  float acc[G][4]; // this lane's 4 columns (d = 128: over its 8 tokens)
+  float m;                   // running max of this lane's head (lane % 16), base 2
+  float l;                   // sum of its weights over this lane's tokens
+  float vref;                // acc is in units of this V row scale (wave-uniform; 0 at the start)
+  f32x4 acc[D / 16];         // O tiles: heads 4 (l / 16) + i, column (ct, l % 16)
 };
-
-template <int D>
-__device__ __forceinline__ void load8(KV8Regs<D>& r, const uint8_t* __restrict__ kt,
-                                      const uint8_t* __restrict__ vt,
-                                      const float* __restrict__ kst,
-                                      const float* __restrict__ vst, int lane) {
-  const int row = lane & 15, grp = lane >> 4;
-#pragma unroll
-  for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2)
-    r.k[c2] = *reinterpret_cast<const uint4*>(kt + row * D + 64 * c2 + 16 * grp);
-  r.ks = *reinterpret_cast<const float4*>(kst + 4 * grp);
-  r.vs = *reinterpret_cast<const float4*>(vst + 4 * grp);
-  if constexpr (V8Layout<D>::HALF) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)  // token 8 (lane / 32) + j, columns 4 (lane % 32) ..
-      r.v[j] = *reinterpret_cast<const uint32_t*>(vt + (8 * (lane >> 5) + j) * D + 4 * (lane & 31));
-  } else {
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-      r.v[t] = *reinterpret_cast<const uint32_t*>(vt + t * D + 4 * lane);
-  }
-}
 
 // The same block through raw buffer resources (codes of K and V, 16 row
 // scales each); resources of 0 bytes read nothing and give zeros, so the
@@ -206,6 +191,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc8(const void* base, uint32
 
 template <int D>
 __device__ __forceinline__ void load8(KV8Regs<D>& r, const Block8Rsrc& t, int lane) {
+  constexpr int VB = V8Layout<D>::VB;
   const int row = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int c2 = 0; c2 < KV8Regs<D>::K16; ++c2)
@@ -213,15 +199,20 @@ __device__ __forceinline__ void load8(KV8Regs<D>& r, const Block8Rsrc& t, int la
         uint4, __builtin_amdgcn_raw_buffer_load_b128(t.k, row * D + 64 * c2 + 16 * grp, 0, 0));
   r.ks = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(t.ks, 16 * grp, 0, 0));
   r.vs = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(t.vs, 16 * grp, 0, 0));
-  if constexpr (V8Layout<D>::HALF) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      r.v[j] = __builtin_amdgcn_raw_buffer_load_b32(
-          t.v, (8 * (lane >> 5) + j) * D + 4 * (lane & 31), 0, 0);
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < 16; ++tt)
-      r.v[tt] = __builtin_amdgcn_raw_buffer_load_b32(t.v, tt * D + 4 * lane, 0, 0);
+  for (int e = 0; e < 4; ++e) {
+    const int off = (4 * grp + e) * D + VB * row;
+    if constexpr (VB == 8) {
+      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(t.v, off, 0, 0));
+      r.v[e][0] = x.x;
+      r.v[e][1] = x.y;
+    } else {
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t.v, off, 0, 0));
+      r.v[e][0] = x.x;
+      r.v[e][1] = x.y;
+      r.v[e][2] = x.z;
+      r.v[e][3] = x.w;
+    }
   }
 }
 
@@ -229,26 +220,26 @@ template <int D, int G>
 __device__ __forceinline__ void wave8_init(Wave8<D, G>& st) {
   st.m = -__builtin_huge_valf();
   st.l = 0.f;
+  st.vref = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st.acc[h][e] = 0.f;
+  for (int ct = 0; ct < D / 16; ++ct) st.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Scores on the matrix cores (codes converted to fp16 pairs, exact), the K
-// row scales, lazy-max online softmax, weights (times the V row scales over
-// the block's largest) to LDS as pairs of consecutive tokens; returns the
-// block's largest V scale (wave-uniform) for block_pv8.
+// row scales, lazy-max online softmax; the weights times the V row scales
+// over the block's largest, as fp16 pairs in pw: the A fragment of P.V (the
+// scores' output layout puts head l % 16 and tokens 4 (l / 16) .. +3 in lane
+// l, which is what the A operand asks for).  Returns the block's largest V
+// scale (wave-uniform) for block_pv8.
 // knew: when not null, the codes of the K row appended in this step for
 // position ctx - 1 (LDS), with its K and V scales ksnew, vsnew; they replace
 // that row of the block holding ctx - 1.
 template <int D, int G>
 __device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs,
                                                Wave8<D, G>& st, int tok0, int ctx,
-                                               float scale_log2, uint32_t* __restrict__ p_lds,
+                                               float scale_log2, uint2& pw,
                                                const uint8_t* knew, float ksnew, float vsnew,
                                                int lane) {
-  constexpr int GP = (G + 3) & ~3;
   static_assert(G <= 16, "one MFMA column per query head");
   const int row = lane & 15, grp = lane >> 4;
   const float kNegInf = -__builtin_huge_valf();
@@ -309,13 +300,15 @@ __device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs
     const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
     st.l *= alpha;
     st.m = mn;
+    // O rows are heads 4 (l / 16) + i here: their factors from the lanes
+    // that hold those heads' scores (alpha is 1 for heads past G)
+    float a[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ah = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+    for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[h][e] *= ah;
-    }
+    for (int ct = 0; ct < D / 16; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[ct][i] *= a[i];
   }
   const float inv_vmax = vmax > 0.f ? 1.f / vmax : 0.f;  // a power of two: exact
   const float neg_m = st.m == kNegInf ? 0.f : -st.m;
@@ -323,70 +316,77 @@ __device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] + neg_m);
   st.l += (p[0] + p[1]) + (p[2] + p[3]);
-  const uint32_t pp0 = pack_h2_rtz(p[0] * (vsv[0] * inv_vmax), p[1] * (vsv[1] * inv_vmax));
-  const uint32_t pp1 = pack_h2_rtz(p[2] * (vsv[2] * inv_vmax), p[3] * (vsv[3] * inv_vmax));
-  if (row < G) {
-    p_lds[(2 * grp) * GP + row] = pp0;
-    p_lds[(2 * grp + 1) * GP + row] = pp1;
-  }
-  wave_fence();
+  pw.x = pack_h2_rtz(p[0] * (vsv[0] * inv_vmax), p[1] * (vsv[1] * inv_vmax));
+  pw.y = pack_h2_rtz(p[2] * (vsv[2] * inv_vmax), p[3] * (vsv[3] * inv_vmax));
   return vmax;
 }
 
+// P.V on the matrix cores: O (heads x d) += P (heads x 16 tokens) V (16
+// tokens x d), one 16 x 16 x 16 product per column tile.  The B fragment of
+// tile ct is byte ct of each of the lane's four token chunks: a 4 x 4 byte
+// transpose (v_perm_b32) of one 32-bit word per token gives four tiles'
+// codes, each converted to four fp16 values (exact).
 // vnew: when not null, the codes of the V row appended for position ctx - 1.
 template <int D, int G>
 __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int tok0, int ctx,
-                                          const uint32_t* __restrict__ p_lds, float vmax,
-                                          const uint8_t* vnew, int lane) {
-  constexpr int GP = (G + 3) & ~3;
-  constexpr bool HALF = V8Layout<D>::HALF;
-  constexpr int TOK = V8Layout<D>::TOK;
-  const int base = HALF ? 8 * (lane >> 5) : 0;  // first token of this lane's v[]
+                                          const uint2& pw, float vmax, const uint8_t* vnew,
+                                          int lane) {
+  constexpr int VB = V8Layout<D>::VB, VW = V8Layout<D>::VW;
+  const int row = lane & 15, grp = lane >> 4;
   if (vnew != nullptr && tok0 + 16 >= ctx) {
-    const int tn = ctx - 1 - tok0 - base;  // index in this lane's v[] (may be outside)
-    if (tn >= 0 && tn < TOK) {
-      // one bit per token, tested with constant j: keeps r.v in registers
-      const uint32_t hit = 1u << tn;
-      const uint32_t nv =
-          *reinterpret_cast<const uint32_t*>(vnew + 4 * (HALF ? (lane & 31) : lane));
+    const int tn = ctx - 1 - tok0 - 4 * grp;  // this lane's token holding ctx - 1 (may be outside)
+    if (tn >= 0 && tn < 4) {
+      uint32_t nv[VW];
 #pragma unroll
-      for (int j = 0; j < TOK; ++j)
-        if (hit & (1u << j)) r.v[j] = nv;
+      for (int w = 0; w < VW; ++w) nv[w] = reinterpret_cast<const uint32_t*>(vnew + VB * row)[w];
+      // constant indices keep r.v in registers
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e == tn)
+#pragma unroll
+          for (int w = 0; w < VW; ++w) r.v[e][w] = nv[w];
     }
   }
   // code 0 = +0 for rows past the context: stale rows never leak (a select on
   // every block, no branch: a branch around the buffer's registers would make
   // the compiler copy them and wait for every load in flight)
 #pragma unroll
-  for (int j = 0; j < TOK; ++j) r.v[j] = tok0 + base + j < ctx ? r.v[j] : 0u;
-  float tmp[G][4];
+  for (int e = 0; e < 4; ++e) {
+    const bool valid = tok0 + 4 * grp + e < ctx;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tmp[h][e] = 0.f;
-  // LDS pair pi holds tokens 2pi and 2pi + 1: this lane's pairs are its
-  // v[2m], v[2m + 1] at pi = base / 2 + m.
-#pragma unroll
-  for (int m = 0; m < TOK / 2; ++m) {
-    const int pi = base / 2 + m;
-    uint32_t pr[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
-    // bytes {a0, b0, a1, b1} and {a2, b2, a3, b3}: token pairs per column
-    const uint32_t x01 = __builtin_amdgcn_perm(r.v[2 * m + 1], r.v[2 * m], 0x05010400u);
-    const uint32_t x23 = __builtin_amdgcn_perm(r.v[2 * m + 1], r.v[2 * m], 0x07030602u);
-    const uint32_t col[4] = {fp8x2_to_h2<false>(x01), fp8x2_to_h2<true>(x01),
-                             fp8x2_to_h2<false>(x23), fp8x2_to_h2<true>(x23)};
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tmp[h][e] = dot2(pr[h], col[e], tmp[h][e]);
+    for (int w = 0; w < VW; ++w) r.v[e][w] = valid ? r.v[e][w] : 0u;
   }
+  // acc moves to units of this block's largest V scale when it differs from
+  // the last block's (a power-of-two ratio for scales the append writes:
+  // exact); the weights are already relative to it.
+  if (vmax > 0.f && vmax != st.vref) {  // the same in every lane
+    const float ratio = st.vref / vmax;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int ct = 0; ct < D / 16; ++ct)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st.acc[h][e] = __builtin_fmaf(tmp[h][e], vmax, st.acc[h][e]);
-  wave_fence();
+      for (int i = 0; i < 4; ++i) st.acc[ct][i] *= ratio;
+    st.vref = vmax;
+  }
+  const f16x4 a = __builtin_bit_cast(f16x4, pw);
+#pragma unroll
+  for (int w = 0; w < VW; ++w) {
+    // bytes {t0.c, t1.c, ...} of words x0..x3 (tokens 0..3), c = 0..3
+    const uint32_t x0 = r.v[0][w], x1 = r.v[1][w], x2 = r.v[2][w], x3 = r.v[3][w];
+    const uint32_t lo01 = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // t0.0 t1.0 t0.1 t1.1
+    const uint32_t hi01 = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // t0.2 t1.2 t0.3 t1.3
+    const uint32_t lo23 = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+    const uint32_t col[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u),
+                             __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x05040100u),
+                             __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint2 b = {fp8x2_to_h2<false>(col[c]), fp8x2_to_h2<true>(col[c])};
+      st.acc[4 * w + c] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          a, __builtin_bit_cast(f16x4, b), st.acc[4 * w + c], 0, 0, 0);
+    }
+  }
 }
 
 // APPEND: the step's decode tokens are quantized and appended by this kernel
@@ -398,7 +398,7 @@ __device__ __forceinline__ void block_pv8(KV8Regs<D>& r, Wave8<D, G>& st, int to
 // slot_mapping[i] at its end (nothing when the slot is negative or beyond the
 // pool) -- the same result as the append kernel followed by the attention.
 template <int D, int G, bool APPEND>
-__global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
+__global__ __launch_bounds__(64 * kWaves, D == 128 ? 2 : 1) void paged_decode_fp8_kernel(
     const uint16_t* __restrict__ q, uint8_t* __restrict__ k_codes,
     uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
     float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
@@ -408,14 +408,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
   constexpr int EPL = D / 64;
-  constexpr int GP = (G + 3) & ~3;
-  // blocks in flight per wave (4 KiB each at d = 128, 8 KiB at d = 256),
-  // as many as fit in 256 registers without spilling
-  constexpr int NBUF = D == 128 ? (G <= 2 ? 4 : (G <= 6 ? 3 : 2)) : (G <= 4 ? 2 : 1);
+  // Blocks in flight per wave (4 KiB each at d = 128, 8 KiB at d = 256).
+  // Measured on MI355X: at d = 128 two per wave at two waves per SIMD beat
+  // three or four (and one block at four waves per SIMD, which loses on
+  // ragged batches); at d = 256 the 16 O tiles leave room for two blocks
+  // only at one wave per SIMD, which beats one block at two.
+  constexpr int NBUF = 2;
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_m[kWaves][G];
   __shared__ float s_l[kWaves][G];
-  __shared__ uint32_t s_p[kWaves][8 * GP];
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
   __shared__ __attribute__((aligned(16))) uint8_t s_newc[2][APPEND ? D : 16];  // K, V codes
   __shared__ float s_news[2];                                                // their scales
@@ -472,9 +473,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
     load8<D>(r, t, lane);
   };
 
+  // The first blocks' loads in the same order as the loop issues them (the
+  // scheduler may not move one across another block's): the wait counts at
+  // the loop top hold for both ways in, and stay deep.
   KV8Regs<D> buf[NBUF];
 #pragma unroll
-  for (int j = 0; j < NBUF; ++j) load_block(buf[j], j);
+  for (int j = 0; j < NBUF; ++j) {
+    load_block(buf[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int k = 0; k < (QCH + 255) / 256; ++k)
     if (tid + 256 * k < QCH) reinterpret_cast<uint4*>(s_q)[tid + 256 * k] = qstage[k];
@@ -515,46 +522,48 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_fp8_kernel(
   auto tok_of = [&](int kk) { return (b0 + wave + kWaves * kk) * 16; };
   // NBUF blocks per trip with no exit in its middle (with one, the compiler
   // sinks loads into the continuing path and the wait counts at the top of
-  // the loop drain the prefetch); the last nbw % NBUF blocks after it.
+  // the loop drain the prefetch); the last 1 .. NBUF blocks after it.  The
+  // appended row can only be in the wave's last block, so only the blocks
+  // after the loop carry the substitution (fewer registers in the loop).
   int k = 0;
-  for (; k + NBUF <= nbw; k += NBUF) {
+  for (; k + NBUF < nbw; k += NBUF) {
 #pragma unroll
     for (int j = 0; j < NBUF; ++j) {
+      uint2 pw;
       const float vmax = block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2,
-                                             s_p[wave], knew, ksnew, vsnew, lane);
-      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, vnew, lane);
+                                             pw, nullptr, 0.f, 0.f, lane);
+      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, pw, vmax, nullptr, lane);
       load_block(buf[j], k + j + NBUF);
     }
   }
 #pragma unroll
-  for (int j = 0; j + 1 < NBUF; ++j) {
+  for (int j = 0; j < NBUF; ++j) {
     if (k + j < nbw) {
+      uint2 pw;
       const float vmax = block_scores8<D, G>(buf[j], s_q, st, tok_of(k + j), ctx, scale_log2,
-                                             s_p[wave], knew, ksnew, vsnew, lane);
-      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, s_p[wave], vmax, vnew, lane);
+                                             pw, knew, ksnew, vsnew, lane);
+      block_pv8<D, G>(buf[j], st, tok_of(k + j), ctx, pw, vmax, vnew, lane);
     }
   }
 
-  // The wave's per-head totals to LDS (the two token halves' columns added
-  // at d = 128); then merge the 4 waves.
+  // The wave's per-head totals to LDS (O tiles back to absolute units and
+  // to d = VB n + ct); then merge the 4 waves.
   float lw = st.l;
   lw += __shfl_xor(lw, 16);
   lw += __shfl_xor(lw, 32);
-  if (lane < 16 && lane < G) {
+  if (lane < G) {
     s_m[wave][lane] = st.m;
     s_l[wave][lane] = lw;
   }
+  {
+    constexpr int VB = V8Layout<D>::VB;
+    const int row = lane & 15, grp = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if constexpr (V8Layout<D>::HALF) {
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * grp + i;
+      if (h < G)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st.acc[h][e] += __shfl_xor(st.acc[h][e], 32);
-      if (lane < 32)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_acc[wave][h][4 * lane + e] = st.acc[h][e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_acc[wave][h][4 * lane + e] = st.acc[h][e];
+        for (int ct = 0; ct < VB; ++ct) s_acc[wave][h][VB * row + ct] = st.acc[ct][i] * st.vref;
     }
   }
   __syncthreads();
