@@ -152,12 +152,14 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
   const int kt_begin = split * per_split;
   const int kt_end = min(kt_begin + per_split, num_kv_tiles);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in all its lanes
   const int lrow = lane & 15, lgrp = lane >> 4;
   // This lane's query row (rows past the chunk end reuse the last row; not
   // written): token my_row of the chunk, for heads my_head + hh.
   const int my_row_raw = tile_row0 + 16 * wave + lrow;
   const bool row_valid = my_row_raw < rows;
+  const bool wave_live = tile_row0 + 16 * wave < rows;  // the same in all lanes of the wave
   const int my_rr = row_valid ? my_row_raw : rows - 1;
   const int my_row = PACK ? my_rr / G : my_rr;
   const int my_head = PACK ? h0 + (my_rr - my_row * G) : h0;
@@ -331,6 +333,9 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
     store_tile(next);
     if (kt + 1 < kt_end) load_tile(next, kt + 1);  // in flight during this tile's math
     __syncthreads();
+    // A wave whose 16 rows are all past the row space (packed short chunks:
+    // n G rows of the 64) only stages tiles: no fragment reads, no math.
+    if (!wave_live) continue;
 
     // S^T = K Q^T: s[hh][t][e] = score of head h0+hh, query row lrow, with
     // token tok0 + 16t + 4*lgrp + e.  Each K fragment feeds HPW MFMAs.
