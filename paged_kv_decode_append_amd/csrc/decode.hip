@@ -17,26 +17,23 @@
 //   longest work starts first and short sequences fill the gaps behind it
 //   (longest-first list scheduling by the hardware dispatcher).
 //   Blocks of a partition are dealt round-robin to its waves; each wave
-//   fetches all its block ids with one vector load and keeps about 16 KiB of
-//   K/V in flight: at d = 128 block f+8 is loaded into block f's registers
-//   in two halves (K once f's scores are done, V after f's P.V), at d = 256
-//   one block (16 KiB) is loaded ahead into a second buffer.
+//   fetches all its block ids with one vector load and keeps two blocks
+//   (16 KiB) in flight: at d = 128 block k+2 is loaded into block k's
+//   registers in two halves (K once k's scores are done, V after its P.V),
+//   at d = 256 one block is loaded ahead into a second buffer.
 //
-// Per block (16 tokens x d) and wave:
-//   K layout: D/16 lanes share one token row, each lane holding 16 of its
-//     d values (two 16-byte chunks), so a K load instruction reads whole
-//     128-byte runs of rows.  q.k is 8 packed fp16 dot products
-//     (v_dot2_f32_f16, fp32 accumulate) per head with the query fragments
-//     read from LDS, then a DPP butterfly inside the lane group.
-//   Online softmax, base 2: scores are scaled by scale*log2(e); the running
-//     max m is wave-uniform and only raised when a score exceeds it by more
-//     than 8 (then the accumulators are rescaled), so weights p = 2^(s-m)
-//     stay in (0, 256] and the common case does no rescale.
-//   V layout: every lane owns d/64 output elements of all 16 tokens, so the
-//     P.V accumulation needs no cross-lane reduction.  The weights travel
-//     from the K layout to all lanes through a small per-wave LDS buffer as
-//     fp16 pairs of tokens (the two tokens a lane group scores in
-//     consecutive K steps), and P.V is again v_dot2_f32_f16 over those pairs.
+// Per block (16 tokens x d) and wave (decode_block.h):
+//   Scores S^T = K Q^T on the matrix cores: K straight from the block as the
+//     A operand, the G query rows from LDS as B; lane l gets head l % 16 for
+//     4 tokens.
+//   Online softmax, base 2: scores are scaled by scale*log2(e); each head's
+//     running max m is only raised when a score exceeds it by more than 8
+//     (then its accumulators are rescaled), so weights p = 2^(s-m) stay in
+//     (0, 256] and the common case does no rescale.
+//   P.V: at d = 128 on the matrix cores as well (P straight from the
+//     scores' registers, V loaded in the B layout); at d = 256 as packed
+//     fp16 dot products with the weights passed through a per-wave LDS
+//     buffer.
 //   Masking is by select: positions >= ctx get score -inf and their V rows
 //   are zeroed before use, so stale or NaN-poisoned slots never leak.
 // At the end the 4 waves' (m, l, acc) merge through LDS; a sequence with a

@@ -17,11 +17,17 @@
 //   by more than kRescaleSlack (a wave vote; then the head's accumulators are
 //   rescaled), so weights p = 2^(s-m) stay in (0, 256] and the common case
 //   needs no cross-lane traffic at all.
-// V layout: every lane owns d/64 output elements of all 16 tokens, so the
-//   P.V accumulation needs no cross-lane reduction.  The weights travel from
-//   the score layout to all lanes through a small per-wave LDS buffer as
-//   fp16 pairs of consecutive tokens, and P.V is v_dot2_f32_f16 over those
-//   pairs (the VALU part, whose layout matches the cache's rows).
+// P.V at d = 128 on the matrix cores too: O = P V with heads as rows, one
+//   v_mfma_f32_16x16x16_f16 per 16-column tile of d.  The scores' layout
+//   (head l % 16, tokens 4 (l / 16) .. +3 in lane l) is P's A fragment as it
+//   stands, so the weights stay in registers.  Lane l loads V of tokens
+//   4 (l / 16) .. +3 at columns 8 (l % 16) .. +7 (one 16-byte load per
+//   token), and one v_perm_b32 per token pair builds a column tile's B
+//   fragment: output column n of tile ct is d = 8 n + ct.
+// At d = 256 (16 such tiles would need 64 more registers): every lane owns
+//   d/64 output elements of all 16 tokens, the weights travel from the score
+//   layout to all lanes through a small per-wave LDS buffer as fp16 pairs of
+//   consecutive tokens, and P.V is v_dot2_f32_f16 over those pairs.
 // Masking is by select: positions >= ctx get score -inf and their V rows are
 //   zeroed before use, so stale or NaN-poisoned slots never leak.
 #pragma once
@@ -31,13 +37,13 @@
 namespace pkv {
 namespace decode_block {
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kRescaleSlack = 8.f;  // lazy max: rescale only past m + 8 (base 2)
 
 template <int D> struct VFrag;
-template <> struct VFrag<128> { typedef uint32_t T; };
 template <> struct VFrag<256> { typedef uint2 T; };
 
 template <int D>
@@ -46,6 +52,12 @@ struct KVRegs {
   uint4 k[KC];                       // token row lane % 16, columns 32c + 8 (lane / 16) .. +7
   typename VFrag<D>::T v[16];
 };
+template <>
+struct KVRegs<128> {
+  static constexpr int KC = 4;
+  uint4 k[KC];
+  uint4 v[4];  // tokens 4 (lane / 16) + e, columns 8 (lane % 16) .. +7
+};
 
 template <int D, int G>
 struct WaveState {
@@ -53,15 +65,27 @@ struct WaveState {
   float l;              // sum of its weights over this lane's tokens
   float acc[G][D / 64]; // sum of weight * v over this lane's output elements
 };
+template <int G>
+struct WaveState<128, G> {
+  float m;
+  float l;
+  f32x4 acc[8];  // O tiles: heads 4 (lane / 16) + i, column (ct, lane % 16): d = 8 (lane % 16) + ct
+  uint2 pw;      // this block's weights (P's A fragment)
+};
 
 template <int D, int G>
 __device__ __forceinline__ void wave_init(WaveState<D, G>& st) {
   st.m = -__builtin_huge_valf();
   st.l = 0.f;
+  if constexpr (D == 128) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int ct = 0; ct < 8; ++ct) st.acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) st.acc[h][e] = 0.f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) st.acc[h][e] = 0.f;
+  }
 }
 
 // The wave's partial (per head: max, weight sum, weighted V columns) into
@@ -78,10 +102,21 @@ __device__ __forceinline__ void wave_store(const WaveState<D, G>& st, float (&s_
     s_m_w[row] = st.m;
     s_l_w[row] = l;
   }
+  if constexpr (D == 128) {
+    const int grp = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * grp + i;
+      if (h < G)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_acc_w[h][EPL * lane + e] = st.acc[h][e];
+        for (int ct = 0; ct < 8; ++ct) s_acc_w[h][8 * row + ct] = st.acc[ct][i];
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc_w[h][EPL * lane + e] = st.acc[h][e];
+  }
 }
 
 template <int D>
@@ -93,9 +128,15 @@ __device__ __forceinline__ void load_k(KVRegs<D>& r, const uint16_t* __restrict_
 
 template <int D>
 __device__ __forceinline__ void load_v(KVRegs<D>& r, const uint16_t* __restrict__ vtile, int lane) {
+  if constexpr (D == 128) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t)
-    r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
+    for (int e = 0; e < 4; ++e)
+      r.v[e] = *reinterpret_cast<const uint4*>(vtile + (4 * (lane >> 4) + e) * D + 8 * (lane & 15));
+  } else {
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+      r.v[t] = *reinterpret_cast<const typename VFrag<D>::T*>(vtile + t * D + (D / 64) * lane);
+  }
 }
 
 // The same loads through a raw buffer resource over one tile (4 KiB at
@@ -118,12 +159,15 @@ __device__ __forceinline__ void load_k(KVRegs<D>& r, __amdgpu_buffer_rsrc_t ktil
 
 template <int D>
 __device__ __forceinline__ void load_v(KVRegs<D>& r, __amdgpu_buffer_rsrc_t vtile, int lane) {
-  const int base = (D / 64) * lane * 2;
+  if constexpr (D == 128) {
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    if constexpr (D == 128)
-      r.v[t] = __builtin_amdgcn_raw_buffer_load_b32(vtile, base + t * D * 2, 0, 0);
-    else
+    for (int e = 0; e < 4; ++e)
+      r.v[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             vtile, ((4 * (lane >> 4) + e) * D + 8 * (lane & 15)) * 2, 0, 0));
+  } else {
+    const int base = (D / 64) * lane * 2;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
       r.v[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vtile, base + t * D * 2, 0, 0));
   }
 }
@@ -143,7 +187,8 @@ __device__ __forceinline__ void pv_dword(float (&acc)[G][2], const uint32_t (&pr
 }
 
 // One 16-token block, first half: scores on the matrix cores, lazy-max online
-// softmax, weights to the wave's LDS buffer (pair pi = tokens 2pi, 2pi + 1).
+// softmax, weights to st.pw (d = 128) or to the wave's LDS buffer (d = 256;
+// pair pi = tokens 2pi, 2pi + 1).
 // After it returns the K registers are free (the next K load may target them).
 // tok0 = logical position of the block's first token.
 // qs = the segment's G query rows in LDS ([G][D] fp16).
@@ -193,13 +238,24 @@ __device__ __forceinline__ void block_scores(KVRegs<D>& r, const uint16_t* qs,
     const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
     st.l *= alpha;
     st.m = mn;
-    // head h's factor lives in lane h
+    if constexpr (D == 128) {
+      // O rows are heads 4 grp + i: their factors from the lanes holding them
+      float a[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ah = __builtin_bit_cast(
-          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+      for (int i = 0; i < 4; ++i) a[i] = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-      for (int e = 0; e < D / 64; ++e) st.acc[h][e] *= ah;
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[ct][i] *= a[i];
+    } else {
+      // head h's factor lives in lane h
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ah = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) st.acc[h][e] *= ah;
+      }
     }
   }
   const float neg_m = st.m == kNegInf ? 0.f : -st.m;
@@ -208,46 +264,78 @@ __device__ __forceinline__ void block_scores(KVRegs<D>& r, const uint16_t* qs,
   // l sums exactly the rounded weights that P.V uses
   st.l = dot2(pp0, kOnesH2, st.l);
   st.l = dot2(pp1, kOnesH2, st.l);
-  if (row < G) {
-    p_lds[(2 * grp) * GP + row] = pp0;
-    p_lds[(2 * grp + 1) * GP + row] = pp1;
+  if constexpr (D == 128) {
+    st.pw = uint2{pp0, pp1};
+  } else {
+    if (row < G) {
+      p_lds[(2 * grp) * GP + row] = pp0;
+      p_lds[(2 * grp + 1) * GP + row] = pp1;
+    }
+    wave_fence();
   }
-  wave_fence();
 }
 
-// Second half: P.V from the V registers and the weights in LDS.  Rows of
-// positions >= ctx are zeroed first (select), so stale slots never leak;
-// vnew, when not null, is the V row appended for position ctx - 1 (LDS).
+// Second half: P.V from the V registers and the weights.  Rows of positions
+// >= ctx are zeroed first (select), so stale slots never leak; vnew, when not
+// null, is the V row appended for position ctx - 1 (LDS).
 template <int D, int G>
 __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int tok0, int ctx,
                                          const uint32_t* __restrict__ p_lds,
                                          const uint16_t* vnew, int lane) {
-  constexpr int GP = (G + 3) & ~3;
-  if (vnew != nullptr && tok0 + 16 >= ctx) {
-    // one bit per token row, tested with constant t: keeps r.v in registers
-    const uint32_t hit = 1u << (ctx - 1 - tok0);
-    const typename VFrag<D>::T nv =
-        *reinterpret_cast<const typename VFrag<D>::T*>(vnew + (D / 64) * lane);
+  if constexpr (D == 128) {
+    const int row = lane & 15, grp = lane >> 4;
+    // The appended row and the rows past the context by select only: a
+    // branch around the buffer's registers makes the compiler wait for every
+    // load in flight.
+    uint4 nv = {0u, 0u, 0u, 0u};
+    int tn = -1;  // this lane's token (0..3) holding ctx - 1, if any
+    if (vnew != nullptr && tok0 + 16 >= ctx) {
+      tn = ctx - 1 - tok0 - 4 * grp;
+      nv = *reinterpret_cast<const uint4*>(vnew + 8 * row);
+    }
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      if (hit & (1u << t)) r.v[t] = nv;
-  }
-  if (tok0 + 16 > ctx) {
+    for (int e = 0; e < 4; ++e) {
+      const uint4 x = e == tn ? nv : r.v[e];
+      r.v[e] = tok0 + 4 * grp + e < ctx ? x : uint4{0u, 0u, 0u, 0u};
+    }
+    // O += P V: tile ct takes the low (even ct) or high half of word ct / 2
+    // of each token's 8 columns
+    const f16x4 a = __builtin_bit_cast(f16x4, st.pw);
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
-      if (tok0 + t >= ctx) r.v[t] = typename VFrag<D>::T{};
-  }
-
-  // P.V: pair pi holds tokens 2pi and 2pi + 1.
+    for (int ct = 0; ct < 8; ++ct) {
+      const int w = ct >> 1;
+      const uint32_t sel = (ct & 1) ? 0x07060302u : 0x05040100u;
+      auto word = [&](const uint4& v) {
+        return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+      };
+      const uint2 b = {__builtin_amdgcn_perm(word(r.v[1]), word(r.v[0]), sel),
+                       __builtin_amdgcn_perm(word(r.v[3]), word(r.v[2]), sel)};
+      st.acc[ct] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, __builtin_bit_cast(f16x4, b),
+                                                         st.acc[ct], 0, 0, 0);
+    }
+  } else {
+    constexpr int GP = (G + 3) & ~3;
+    if (vnew != nullptr && tok0 + 16 >= ctx) {
+      // one bit per token row, tested with constant t: keeps r.v in registers
+      const uint32_t hit = 1u << (ctx - 1 - tok0);
+      const typename VFrag<D>::T nv =
+          *reinterpret_cast<const typename VFrag<D>::T*>(vnew + (D / 64) * lane);
 #pragma unroll
-  for (int pi = 0; pi < 8; ++pi) {
-    const int ta = 2 * pi, tb = ta + 1;
-    uint32_t pr[G];
+      for (int t = 0; t < 16; ++t)
+        if (hit & (1u << t)) r.v[t] = nv;
+    }
+    if (tok0 + 16 > ctx) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
-    if constexpr (D == 128) {
-      pv_dword<G>(reinterpret_cast<float(&)[G][2]>(st.acc), pr, r.v[ta], r.v[tb]);
-    } else {
+      for (int t = 0; t < 16; ++t)
+        if (tok0 + t >= ctx) r.v[t] = typename VFrag<D>::T{};
+    }
+    // P.V: pair pi holds tokens 2pi and 2pi + 1.
+#pragma unroll
+    for (int pi = 0; pi < 8; ++pi) {
+      const int ta = 2 * pi, tb = ta + 1;
+      uint32_t pr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pr[h] = p_lds[pi * GP + h];
       float lo[G][2], hi[G][2];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -262,10 +350,9 @@ __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int 
         st.acc[h][2] = hi[h][0]; st.acc[h][3] = hi[h][1];
       }
     }
+    wave_fence();
   }
-  wave_fence();
 }
-
 
 }  // namespace decode_block
 }  // namespace pkv
