@@ -537,6 +537,17 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
     m = ml[2 * lane];
     l = ml[2 * lane + 1];
   }
+  // Every split's o is requested before the weights are known (one memory
+  // round trip, not two); loads of splits past num_splits re-read the last
+  // one (in bounds) and get weight 0.
+  const float* src = part_o + rh * num_splits * D + EPL * lane;
+  float o[kMaxPrefillSplits][EPL];
+#pragma unroll
+  for (int s = 0; s < kMaxPrefillSplits; ++s) {
+    const int sc = min(s, num_splits - 1);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[s][e] = src[(int64_t)sc * D + e];
+  }
   float M = l > 0.f ? m : -__builtin_huge_valf();
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -547,18 +558,11 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  const float* src = part_o + rh * num_splits * D + EPL * lane;
-  // loads of splits past num_splits re-read the last one (in bounds, always
-  // issued, so that all loads are in flight together) and get weight 0
 #pragma unroll
   for (int s = 0; s < kMaxPrefillSplits; ++s) {
-    const int sc = min(s, num_splits - 1);
     const float ws = s < num_splits ? __shfl(w, s) : 0.f;
-    float o[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = src[(int64_t)sc * D + e];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += ws > 0.f ? ws * o[e] : 0.f;
+    for (int e = 0; e < EPL; ++e) acc[e] += ws > 0.f ? ws * o[s][e] : 0.f;
   }
   uint16_t* dst = out + (first_row * num_q_heads + rh) * D + EPL * lane;
   const float inv = W > 0.f ? 1.f / W : 0.f;
