@@ -39,8 +39,9 @@
 //     when it changes from one block to the next; the softmax denominator
 //     sums the unscaled weights.
 // On MI355X this kernel is bound by its per-block arithmetic more than by
-// bytes in flight: with P.V as packed dot products (the fp16 kernel's way) it
-// ran 40% slower at B = 256, ctx 512 than with P.V removed altogether.
+// bytes in flight: with P.V as packed fp16 dot products over weights passed
+// through LDS it ran 40% slower at B = 256, ctx 512 than with P.V removed
+// altogether.
 #include <algorithm>
 #include <climits>
 
