@@ -396,7 +396,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl) if fused and args.kv_dtype == "fp16" else None,
+            # the committed counters were taken on the workload's own sizes,
+            # fused, fp16, with the automatic plan
+            "traffic": (measured_traffic(wl) if fused and args.kv_dtype == "fp16"
+                        and not args.batch and not args.ctx and args.partition == 0
+                        and args.schedule == "auto" else None),
             "kernel": kernel,
             "alg_bytes_per_launch": alg_bytes,
             "launch_us": round(attn_us, 2),
