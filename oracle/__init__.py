@@ -9,6 +9,7 @@ knows nothing of block tables.
 
 Functions (each cites what it follows in the C source):
   slot_mapping, kv_append, paged_attention, paged_attention_fp8,
+  paged_attention_f64,
   attention_partial, lse_merge, half_to_float64.
 Submodules: ``fp8`` (E4M3 codes and the per-row quantization of an fp8
 cache), ``scheduler`` (plain model of the per-pass scheduler), ``dense``.
@@ -157,9 +158,20 @@ def paged_attention_fp8(q, k_codes, v_codes, k_scales, v_scales, block_tables, c
     """fp64 attention [T, Hq, d] over an fp8 cache: the pools are dequantized
     (oracle.fp8.dequantize, exact) and attended as in paged_attention."""
     from . import fp8
+    kd = fp8.dequantize(k_codes, k_scales)
+    vd = fp8.dequantize(v_codes, v_scales)
+    return paged_attention_f64(q, kd, vd, block_tables, context_lens, query_start_loc, scale,
+                               seq_subset=seq_subset)
+
+
+def paged_attention_f64(q, k_pool, v_pool, block_tables, context_lens, query_start_loc,
+                        scale: float, seq_subset=None):
+    """fp64 attention [T, Hq, d] over pools already held as float64
+    [NB, Hkv, bs, d] (a dequantized fp8 cache): the same gather-then-attend
+    as paged_attention, with fp16 queries."""
     qb = _bits(q)
-    kd = np.ascontiguousarray(fp8.dequantize(k_codes, k_scales))
-    vd = np.ascontiguousarray(fp8.dequantize(v_codes, v_scales))
+    kd = _c(k_pool, np.float64)
+    vd = _c(v_pool, np.float64)
     bt = _c(block_tables, np.int32)
     ctx = _c(context_lens, np.int32)
     qsl = None if query_start_loc is None else _c(query_start_loc, np.int32)

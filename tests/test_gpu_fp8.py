@@ -224,27 +224,16 @@ def test_short_chunk_splits_over_an_fp8_cache(part):
 
 def test_qwen_mixed_full_size_fp8():
     """64 decodes + a 512-row chunk over an 8,192-token prefix over an fp8
-    cache: sampled decode sequences, and chunk rows sampled across all 8 row
-    tiles, each checked as the query attending positions [0, its position]."""
+    cache: every decode sequence and every row of the chunk checked."""
     wl = workloads.qwen_mixed()
     t = _fp8_cache(wl, layer=5, poison=False)
     t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
     _, out = _run(wl, t, fused=True)
     kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
-    got, q = out.cpu().numpy(), host_bits(t["q"])
-    subset = [0, 17, 40, 63]
-    ref = oracle.paged_attention_fp8(q, kc, vc, ks, vs, wl.block_tables, wl.context_lens, qsl,
-                                     wl.scale, seq_subset=subset)
-    errs = assert_close(got[subset], ref[subset], "qwen_mixed fp8 decodes")
-    seq = wl.num_seqs - 1
-    rows = np.array([0, 1, 15, 16, 63, 64, 127, 200, 255, 256, 300, 383, 448, 500, 510, 511])
-    n, ctx, r0 = wl.new_tokens[seq], wl.context_lens[seq], wl.query_start_loc[seq]
-    sub_ctx = (ctx - n + rows + 1).astype(np.int32)
-    sub_bt = np.repeat(wl.block_tables[seq:seq + 1], len(rows), axis=0)
-    sub_ref = oracle.paged_attention_fp8(q[r0 + rows], kc, vc, ks, vs, sub_bt, sub_ctx, None,
-                                         wl.scale)
-    e2 = assert_close(got[r0 + rows], sub_ref, "qwen_mixed fp8 chunk rows")
-    _report("qwen_mixed fp8 layer 5", (max(errs[0], e2[0]), max(errs[1], e2[1])))
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    errs = assert_close(out.cpu().numpy(), ref, "qwen_mixed fp8")
+    _report("qwen_mixed fp8 layer 5 (64 decodes, all 512 chunk rows)", errs)
 
 
 @pytest.mark.parametrize("kind", ["decode", "short", "long"])
@@ -287,20 +276,76 @@ def test_row_scales_spanning_a_wide_range(kind):
 @pytest.mark.parametrize("name", ["qwen_uniform", "qwen_ragged", "qwen_spec"])
 def test_full_size_fp8(name):
     """One layer of the 28-layer workloads over an fp8 cache (qwen_spec:
-    64 sequences verifying 4 tokens each, on the packed-row kernel), sampled
-    sequences against the oracle."""
+    64 sequences verifying 4 tokens each, on the packed-row kernel), every
+    sequence against the oracle."""
     wl = workloads.WORKLOADS[name]()
     t = _fp8_cache(wl, layer=3, poison=False)
     t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
     _, out = _run(wl, t, fused=True)
     kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
-    subset = [0, 1, 17, 40, wl.num_seqs - 1]
     ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
-                                     wl.context_lens, qsl, wl.scale, seq_subset=subset)
-    rows = np.concatenate([np.arange(wl.query_start_loc[i], wl.query_start_loc[i + 1])
-                           for i in subset])
-    errs = assert_close(out.cpu().numpy()[rows], ref[rows], name)
-    _report(f"{name} fp8 layer 3", errs)
+                                     wl.context_lens, qsl, wl.scale)
+    errs = assert_close(out.cpu().numpy(), ref, name)
+    _report(f"{name} fp8 layer 3 (all {wl.num_seqs} sequences)", errs)
+
+
+def _dequantized_sequence(wl, i, kc, vc, ks, vs):
+    """Sequence i's blocks of an fp8 cache, dequantized (the oracle's E4M3
+    decoding, applied through a table of its 256 code values) into a compact
+    pool in table order, with the table that reads them there: block
+    relabelling leaves attention unchanged, and the whole 4 GiB-per-layer
+    pool would not fit in fp64."""
+    nb = -(-int(wl.context_lens[i]) // wl.block_size)
+    ids = wl.block_tables[i, :nb]
+    lut = ofp8.e4m3_to_float64(np.arange(256, dtype=np.uint8))
+    kd = lut[kc[ids]] * ks[ids].astype(np.float64)[..., None]
+    vd = lut[vc[ids]] * vs[ids].astype(np.float64)[..., None]
+    table = np.arange(nb, dtype=np.int32)[None, :]
+    return kd, vd, table
+
+
+def test_long_context_full_size_fp8():
+    """long_context (4 x 262,144 tokens, d = 256, 16/4 heads) over an fp8
+    cache at the plan the benchmark runs (256-block partitions: 64 blocks per
+    wave, a block id in every lane), the decode tokens' quantizing append
+    fused: codes and scales bit-exact, all 4 sequences against the oracle."""
+    wl = workloads.long_context()
+    t = _fp8_cache(wl, layer=2, poison=False)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    step, out = _run(wl, t, fused=True)
+    assert step.kv_partition_tokens == 0
+    kc, vc, ks, vs, _ = _append_ref(wl, t0, t)
+    del t0
+    got, q = out.cpu().numpy(), host_bits(t["q"])
+    worst = (0.0, 0.0)
+    for i in range(wl.num_seqs):
+        kd, vd, table = _dequantized_sequence(wl, i, kc, vc, ks, vs)
+        ctx = wl.context_lens[i:i + 1]
+        ref = oracle.paged_attention_f64(q[i:i + 1], kd, vd, table, ctx, None, wl.scale)
+        e = assert_close(got[i:i + 1], ref, f"long_context fp8 sequence {i}")
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+        del kd, vd
+    _report("long_context fp8 layer 2 (all 4 sequences)", worst)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("d,hq,hkv", [(128, 12, 2), (128, 8, 1), (256, 16, 4), (256, 24, 3)])
+def test_long_partitions_over_an_fp8_cache(d, hq, hkv, fused):
+    """4,096-token partitions (256 blocks: 64 per wave, a block id in every
+    lane) over contexts of 4,097 to 9,000 tokens, next to short ones: the
+    partition sizes the long-context plan picks, at contexts the oracle
+    attends in full."""
+    ctx = [4100, 8200, 9000, 5000, 17, 4096, 4097, 8192]
+    wl = workloads.custom("fp8_long_part", ctx, [1] * len(ctx), len(ctx), hq, hkv, d,
+                          seed=hq * d + fused)
+    t = _fp8_cache(wl)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, part=4096, fused=fused)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    errs = assert_close(out.cpu().numpy(), ref, f"fp8 part=4096 d={d} G={hq // hkv}")
+    _report(f"fp8 part=4096 d={d} G={hq // hkv} fused={fused}", errs)
 
 
 @pytest.mark.parametrize("part", [0, 64])
