@@ -340,9 +340,11 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
  *   num_layers              >= 0 (0: nothing is launched)
  *   other arguments         as for pkv_append_attention_step; the one
  *                           workspace serves every layer (stream order).
- * Every argument is checked before the first launch (all layers'
- * descriptors included); the first launch error stops the loop and is
- * returned (the layers before it are enqueued).
+ * Every argument is checked before the first launch: all layers'
+ * descriptors and pointers, and each layer's plan (workspace and schedule
+ * sizes, grid limits -- they depend on its heads and head_dim), so an
+ * argument error enqueues nothing.  The first launch error stops the loop
+ * and is returned (the layers before it are enqueued).
  * Errors: as for pkv_append_attention_step.
  */
 int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,

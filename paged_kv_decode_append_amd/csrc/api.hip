@@ -69,6 +69,10 @@ int from_hip(hipError_t e) {
 
 }  // namespace
 
+namespace pkv {
+void record_hip_error(hipError_t e) { t_last_hip_error = e; }
+}  // namespace pkv
+
 extern "C" {
 
 int pkv_version(void) { return PKV_VERSION; }
@@ -184,8 +188,11 @@ namespace {
 
 // Attention of one layer; with k_new non-null the new tokens' append is done
 // here too: the decode tokens' inside the decode kernel, the prefill tokens'
-// by the append kernel ahead of the prefill kernel.
-int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_new,
+// by the append kernel ahead of the prefill kernel.  With check_only, every
+// check (arguments, plans, workspace and schedule sizes, grid limits) runs
+// and nothing is launched.
+int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new,
+                   const void* v_new,
                    const int64_t* slot_mapping, int32_t num_tokens, const void* q, void* out,
                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                    const int32_t* context_lens, const int32_t* query_start_loc,
@@ -230,6 +237,7 @@ int attention_step(const pkv_kv_cache* cache, const void* k_new, const void* v_n
                                                    max_query_len, kv_partition_tokens);
   const size_t need = workspace_layout(plan, pplan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  if (check_only) return PKV_OK;
   void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
@@ -304,7 +312,7 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
                              int32_t kv_partition_tokens, const void* schedule,
                              size_t schedule_bytes, void* workspace, size_t workspace_bytes,
                              void* stream) {
-  return attention_step(cache, nullptr, nullptr, nullptr, 0, q, out, block_tables,
+  return attention_step(false, cache, nullptr, nullptr, nullptr, 0, q, out, block_tables,
                         max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
                         num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
                         kv_partition_tokens, schedule, schedule_bytes, workspace,
@@ -322,7 +330,7 @@ int pkv_append_attention_step(const pkv_kv_cache* cache, const void* k_new, cons
                               size_t schedule_bytes, void* workspace, size_t workspace_bytes,
                               void* stream) {
   if (!k_new) return PKV_ERR_INVALID_ARG;
-  return attention_step(cache, k_new, v_new, slot_mapping, num_tokens, q, out, block_tables,
+  return attention_step(false, cache, k_new, v_new, slot_mapping, num_tokens, q, out, block_tables,
                         max_blocks_per_seq, context_lens, query_start_loc, num_seqs,
                         num_decode_seqs, num_q_heads, scale, max_context_len, max_query_len,
                         kv_partition_tokens, schedule, schedule_bytes, workspace,
@@ -343,19 +351,21 @@ int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,
   if (num_layers < 0) return PKV_ERR_INVALID_ARG;
   if (num_layers == 0) return PKV_OK;
   if (!caches || !k_new || !v_new || !q || !out) return PKV_ERR_INVALID_ARG;
-  // every layer's descriptor and pointers before the first launch
+  // every layer's descriptor, pointers and plans (workspace and schedule
+  // sizes, grid limits, which depend on its heads and head_dim) before the
+  // first launch
   for (int32_t l = 0; l < num_layers; ++l) {
-    int rc = check_cache(&caches[l]);
+    if (!k_new[l]) return PKV_ERR_INVALID_ARG;
+    const int rc = attention_step(true, &caches[l], k_new[l], v_new[l], slot_mapping, num_tokens,
+                                  q[l], out[l], block_tables, max_blocks_per_seq, context_lens,
+                                  query_start_loc, num_seqs, num_decode_seqs, num_q_heads, scale,
+                                  max_context_len, max_query_len, kv_partition_tokens, schedule,
+                                  schedule_bytes, workspace, workspace_bytes, stream);
     if (rc != PKV_OK) return rc;
-    rc = check_step_shape(num_seqs, num_decode_seqs, num_q_heads, caches[l].num_kv_heads,
-                          caches[l].head_dim, max_context_len, max_query_len,
-                          kv_partition_tokens);
-    if (rc != PKV_OK) return rc;
-    if (!k_new[l] || !v_new[l] || (num_seqs > 0 && (!q[l] || !out[l])))
-      return PKV_ERR_INVALID_ARG;
   }
   for (int32_t l = 0; l < num_layers; ++l) {
-    const int rc = attention_step(&caches[l], k_new[l], v_new[l], slot_mapping, num_tokens, q[l],
+    const int rc = attention_step(false, &caches[l], k_new[l], v_new[l], slot_mapping,
+                                  num_tokens, q[l],
                                   out[l], block_tables, max_blocks_per_seq, context_lens,
                                   query_start_loc, num_seqs, num_decode_seqs, num_q_heads, scale,
                                   max_context_len, max_query_len, kv_partition_tokens, schedule,

@@ -9,6 +9,9 @@
 
 namespace pkv {
 
+// Keeps a HIP error for pkv_last_hip_error on this thread (api.hip).
+void record_hip_error(hipError_t e);
+
 hipError_t launch_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, const int32_t* query_start_loc,
                                int32_t num_seqs, int32_t num_tokens, int64_t* slot_mapping,

@@ -125,7 +125,7 @@ def _layers(caches, L=None, kn=FAKE, vn=FAKE, q=FAKE, out=FAKE, T=4, nseq=4, nde
     ptrs = lambda p: None if p is None else (ctypes.c_void_p * max(len(caches), 1))(*([p] * len(caches)))
     return pkv.lib.pkv_append_attention_layers(arr, L, ptrs(kn), ptrs(vn), FAKE, T, ptrs(q),
                                                ptrs(out), FAKE, maxblk, FAKE, None, nseq, ndec,
-                                               hq, 0.1, mcl, 1, 0, None, 0, None, 0, None)
+                                               hq, 0.1, mcl, 1, 0, None, 0, FAKE, 1 << 30, None)
 
 
 def test_layers_argument_errors_are_found_before_any_launch():
@@ -143,6 +143,23 @@ def test_layers_argument_errors_are_found_before_any_launch():
     assert pkv.lib.pkv_append_attention_layers(None, 2, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 64,
                                                FAKE, None, 4, 4, 12, 0.1, 1024, 1, 0, None, 0,
                                                None, 0, None) == -1
+
+
+def test_layers_plans_are_checked_before_any_launch():
+    """A later layer whose plan needs more workspace than the call brings
+    (d = 256 beside a d = 128 layer, 4 KV heads each) is refused before the
+    first layer is launched: PKV_ERR_WORKSPACE, not the launch error a
+    first layer enqueued without a GPU would give."""
+    small, big = _cache(head_dim=128, kv_heads=4), _cache(head_dim=256, kv_heads=4)
+    need_small = pkv.attention_workspace_size(4, 4, 16, 4, 128, 65536, 1)
+    need_big = pkv.attention_workspace_size(4, 4, 16, 4, 256, 65536, 1)
+    assert need_big > need_small > 0
+    arr = (pkv._Cache * 2)(small, big)
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    rc = pkv.lib.pkv_append_attention_layers(arr, 2, ptrs, ptrs, FAKE, 4, ptrs, ptrs, FAKE, 4096,
+                                             FAKE, None, 4, 4, 16, 0.1, 65536, 1, 0, None, 0,
+                                             FAKE, need_small, None)
+    assert rc == pkv.PKV_ERR_WORKSPACE
 
 
 def test_decode_schedule_size_and_argument_errors():
