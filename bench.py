@@ -9,7 +9,14 @@ pkv_append_attention_step call (the decode tokens are appended inside the
 decode kernel); --separate runs pkv_kv_append + pkv_paged_attention_step.
 Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--separate]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--extra A,B]
+                    [--separate] [--kv-dtype fp16|fp8]
+
+The headline workload (default long_context: 16 layers of 4 sequences at
+262,144 tokens, the largest configuration) is the line's top level; the
+workloads named by --extra (default, with the default headline: qwen_ragged
+and qwen_uniform) are measured in the same run and reported under
+"workloads", each with its own roofline and cpu_baseline.
 
 value      = decode tokens per second of the whole step (query tokens of the
              decode and multi-token-decode sequences x steps / wall time),
@@ -20,14 +27,21 @@ roofline   = the dominant kernel (paged decode + its merge): algorithmic
              duration from HIP events around back-to-back attention
              launches, against the 8 TB/s HBM peak; also against the rate of
              a plain device copy moving the same number of bytes
-             (measured_copy_gbps, frac_of_measured_copy).
+             (measured_copy_gbps, frac_of_measured_copy), and against the
+             read rate of pkv_hbm_read_probe over the same tile size and
+             bytes in a random order in a 4 GiB buffer (read_probe_gbps,
+             frac_of_read_probe).  traffic = HBM bytes per launch from the
+             committed rocprofv3 counter summary named in traffic_source
+             (reported only while the decode kernel's sources still hash to
+             the value recorded there; not measured in this run).
 ms_per_step_median / _min = per-step durations from events between the timed
              steps.
 prefill    = (steps with prefill chunks) the chunks alone timed the same
              way: flops per launch over launch time against the dense fp16
              MFMA peak; query_tokens_per_s counts every new token of the step.
 cpu_baseline = the fp64 CPU oracle, timed on the host on a bounded sample of
-             the same workload (a few layers of the step), scaled to a step.
+             the same workload (a few layers of the step), scaled to a step;
+             with the host's CPU model and the cores the process may use.
 """
 from __future__ import annotations
 
@@ -46,7 +60,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-attn step: KV-read HBM GB/s (% of peak) and decode tokens/s at 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak (no sparsity)
-DEFAULT_WORKLOAD = "qwen_uniform"
+DEFAULT_WORKLOAD = "long_context"
+DEFAULT_EXTRA = ("qwen_ragged", "qwen_uniform")
 
 
 def parse():
@@ -55,6 +70,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated workloads measured in the same run and reported "
+                         "under 'workloads' (default: qwen_ragged,qwen_uniform with the "
+                         "default headline and no overrides; 'none' for none)")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the HBM read-rate probe")
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--batch", type=int, default=0, help="override the batch (uniform / long_context)")
     ap.add_argument("--ctx", type=int, default=0, help="override the context length (uniform / long_context)")
@@ -113,11 +134,12 @@ def streamed_tokens(wl) -> int:
 
 
 def measured_traffic(wl):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary of this workload, or None when there is none or the decode
-    kernel's sources changed since it was taken."""
+    """(HBM bytes per attention launch, summary path) from the committed
+    rocprofv3 counter summary of this workload, or None when there is none
+    or the decode kernel's sources changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"paged_decode_{wl.name}_hbm_traffic.txt")
+    rel = f"profiles/paged_decode_{wl.name}_hbm_traffic.txt"
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
         return None
     fields = dict(line.split(": ", 1) for line in open(path) if ": " in line and not line.startswith(" "))
@@ -127,7 +149,69 @@ def measured_traffic(wl):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields["traffic_bytes_per_launch"]), rel
+
+
+def read_probe_rate(tile_bytes: int, bytes_per_launch: int, seed: int = 0):
+    """GB/s that pkv_hbm_read_probe sustains reading `bytes_per_launch` per
+    launch as whole `tile_bytes` tiles in a random order, from a buffer of at
+    least 4 GiB (far beyond the last-level cache), successive launches taking
+    the next tiles of one permutation.  HIP events on the launch stream."""
+    import torch
+    import paged_kv_decode_append_amd as pkv
+    n = max(1, bytes_per_launch // tile_bytes)
+    ntiles = max(n, (4 << 30) // tile_bytes)
+    base = torch.zeros(ntiles * tile_bytes, dtype=torch.uint8, device="cuda")
+    perm = np.random.default_rng(seed).permutation(ntiles).astype(np.int32)
+    ids = torch.from_numpy(np.concatenate([perm, perm[:n]])).cuda()
+    sink = torch.empty(pkv.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    launches = 10
+    start = 0
+
+    def launch():
+        nonlocal start
+        pkv.hbm_read_probe(base, ids[start:start + n], tile_bytes, sink)
+        start = (start + n) % ntiles
+
+    for _ in range(2):
+        launch()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(launches):
+        launch()
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / launches
+    del base, ids, sink
+    torch.cuda.empty_cache()
+    return {"read_probe_gbps": round(n * tile_bytes / t / 1e9, 1), "read_probe_tile_bytes": tile_bytes,
+            "read_probe_bytes_per_launch": n * tile_bytes}
+
+
+def host_description():
+    """CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        cpus = sorted(os.sched_getaffinity(0))
+    except AttributeError:
+        cpus = list(range(os.cpu_count() or 1))
+    runs, lo = [], None
+    for k, c in enumerate(cpus):
+        if lo is None:
+            lo = c
+        if k + 1 == len(cpus) or cpus[k + 1] != c + 1:
+            runs.append(f"{lo}-{c}" if c != lo else f"{c}")
+            lo = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": len(cpus),
+            "affinity": ",".join(runs)}
 
 
 def measured_copy_rate(nbytes: int) -> float:
@@ -226,39 +310,19 @@ def cpu_baseline(wl, layer_tensors_dev, budget_s: float, kv_dtype: str = "fp16")
         "kind": "oracle",
         "sample": f"{layers} of {wl.num_layers} layers of one {wl.name} step "
                   f"({spent:.1f} s), scaled to a whole step",
+        **host_description(),
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "one GPU only: the benchmark measures a single device; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-
+def measure(args, name: str, with_cpu: bool, overrides=None) -> dict:
+    """One workload: K timed steps, the attention launch's roofline, the
+    prefill chunks' (when the step has them) and the oracle's baseline."""
     import torch
-
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(1)
-    if args.copy_calibration:
-        n = args.copy_calibration
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "copies": 5}))
-        return
-
     import workloads
     import paged_kv_decode_append_amd as pkv
     from paged_kv_decode_append_amd.step import Step
 
-    make = workloads.WORKLOADS[args.workload]
-    overrides = {k: v for k, v in (("layers", args.layers), ("batch", args.batch),
-                                    ("ctx_len", args.ctx)) if v}
-    wl = make(**overrides)
+    wl = workloads.WORKLOADS[name](**(overrides or {}))
     if args.kv_dtype == "fp8":
         layers = [workloads.layer_tensors_fp8(wl, l, device="cuda") for l in range(wl.num_layers)]
         caches = [pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
@@ -278,12 +342,11 @@ def main():
         for c, t, o in zip(caches, layers, outs):
             step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=fused)
 
+    prepared = None
     if args.one_call:
-        if not fused or args.graph:
-            print(json.dumps({"error": "--one-call is the fused eager step; drop --separate/--graph"}))
-            sys.exit(2)
-        run_step = step.prepare_layers([(c, t["q"], t["k_new"], t["v_new"], o)
+        prepared = step.prepare_layers([(c, t["q"], t["k_new"], t["v_new"], o)
                                         for c, t, o in zip(caches, layers, outs)])
+        run_step = prepared
     if args.graph:
         run_step()
         graph = step.capture([(c, t["q"], t["k_new"], t["v_new"], o)
@@ -322,9 +385,9 @@ def main():
             for c, t in zip(caches, layers):
                 pkv.kv_append(c, t["k_new"], t["v_new"], step.slot_mapping)
         ev[r][0].record(stream)
-        if args.one_call:
-            run_step.attend()
-        for c, t, o in zip(caches, layers, outs) if not args.one_call else ():
+        if prepared is not None:
+            prepared.attend()
+        for c, t, o in zip(caches, layers, outs) if prepared is None else ():
             if fused:
                 step.layer(c, t["q"], t["k_new"], t["v_new"], o, fused=True)
             else:
@@ -353,6 +416,31 @@ def main():
     if multi:
         kernel += ("; multi-token decodes on the packed-row MFMA kernel (+ its merge)" +
                    (f" after their {quant}append" if fused else ""))
+    # the committed counters were taken on the workload's own sizes, fused,
+    # fp16, with the automatic plan
+    traffic = (measured_traffic(wl) if fused and args.kv_dtype == "fp16" and not overrides
+               and args.partition == 0 and args.schedule == "auto" else None)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic[0] if traffic else None,
+        "traffic_source": (f"{traffic[1]} (rocprofv3 FETCH_SIZE + WRITE_SIZE of the same kernel "
+                           "sources, scaled by a plain copy's counters; not measured in this run)"
+                           if traffic else None),
+        "kernel": kernel,
+        "alg_bytes_per_launch": alg_bytes,
+        "launch_us": round(attn_us, 2),
+        "measured_copy_gbps": round(copy_gbps, 1),
+        "frac_of_measured_copy": round(achieved / copy_gbps, 4),
+    }
+    if not args.no_read_probe:
+        row_tile = 16 * (wl.head_dim * 2 if args.kv_dtype == "fp16" else wl.head_dim)
+        probe = read_probe_rate(row_tile, alg_bytes)
+        roofline.update(probe)
+        roofline["frac_of_read_probe"] = round(achieved / probe["read_probe_gbps"], 4)
     result = {
         "metric": METRIC,
         "value": round(streamed_tokens(wl) / (ms_per_step * 1e-3), 1),
@@ -366,7 +454,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16",
+        # the arithmetic: fp16 products with fp32 accumulation; fp8 codes are
+        # widened to fp16 (exactly) before they are multiplied
+        "dtype": "fp16" if args.kv_dtype == "fp16" else "fp16 (fp8_e4m3 KV codes widened)",
+        "kv_dtype": "fp16" if args.kv_dtype == "fp16" else "fp8_e4m3",
         "data": "synthetic",
         "config": {
             "workload": wl.name,
@@ -390,30 +481,63 @@ def main():
                        "one library call per step" if args.one_call else
                        "one library call per layer"),
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            # the committed counters were taken on the workload's own sizes,
-            # fused, fp16, with the automatic plan
-            "traffic": (measured_traffic(wl) if fused and args.kv_dtype == "fp16"
-                        and not args.batch and not args.ctx and args.partition == 0
-                        and args.schedule == "auto" else None),
-            "kernel": kernel,
-            "alg_bytes_per_launch": alg_bytes,
-            "launch_us": round(attn_us, 2),
-            "measured_copy_gbps": round(copy_gbps, 1),
-            "frac_of_measured_copy": round(achieved / copy_gbps, 4),
-        },
+        "roofline": roofline,
         "kv_read_gbps_step": round(kv_bytes_step / (ms_per_step * 1e-3) / 1e9, 1),
     }
     if prefill is not None:
         result["query_tokens_per_s"] = round(wl.num_tokens / (ms_per_step * 1e-3), 1)
         result["prefill"] = prefill
-    if not args.no_cpu_baseline:
+    if with_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, layers, args.cpu_budget_s, args.kv_dtype)
+    del layers, caches, outs, step, run_step, prepared
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "one GPU only: the benchmark measures a single device; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}))
+        return
+    if args.one_call and (args.separate or args.graph):
+        print(json.dumps({"error": "--one-call is the fused eager step; drop --separate/--graph"}))
+        sys.exit(2)
+
+    import workloads
+    if args.workload not in workloads.WORKLOADS:
+        print(json.dumps({"error": f"unknown workload {args.workload}"}))
+        sys.exit(2)
+    overrides = {k: v for k, v in (("layers", args.layers), ("batch", args.batch),
+                                    ("ctx_len", args.ctx)) if v}
+    if args.extra is None:
+        extra = list(DEFAULT_EXTRA) if args.workload == DEFAULT_WORKLOAD and not overrides else []
+    else:
+        extra = [w for w in args.extra.split(",") if w and w != "none"]
+    for w in extra:
+        if w not in workloads.WORKLOADS:
+            print(json.dumps({"error": f"unknown workload {w}"}))
+            sys.exit(2)
+    with_cpu = not args.no_cpu_baseline
+    result = measure(args, args.workload, with_cpu, overrides)
+    if extra:
+        result["workloads"] = {w: measure(args, w, with_cpu) for w in extra if w != args.workload}
     print(json.dumps(result), flush=True)
 
 

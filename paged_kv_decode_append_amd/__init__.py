@@ -5,8 +5,9 @@ libpkv.so; torch supplies device memory and the stream.  The names follow
 the C ABI in include/pkv.h without the ``pkv_`` prefix:
 
     slot_mapping, kv_append, attention_workspace_size, decode_schedule_size,
-    decode_schedule, paged_attention_step, append_attention_step, validate_step,
-    status_string, last_hip_error, version
+    decode_schedule, paged_attention_step, append_attention_step,
+    validate_step, hbm_read_probe, status_string,
+    last_hip_error, version
 
 There is no fallback: importing this package without a built libpkv.so
 raises, and every call raises PkvError on a non-OK status.
@@ -33,8 +34,11 @@ EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_hip_error", "pkv_slot_mapping", "pkv_kv_append",
     "pkv_attention_workspace_size", "pkv_decode_schedule_size", "pkv_decode_schedule",
     "pkv_paged_attention_step", "pkv_append_attention_step", "pkv_append_attention_layers",
-    "pkv_validate_step",
+    "pkv_validate_step", "pkv_hbm_read_probe",
 )
+
+# work-groups of pkv_hbm_read_probe (words of its sink)
+PROBE_SINK_WORDS = 2048
 
 
 class PkvError(RuntimeError):
@@ -90,6 +94,7 @@ def _load():
     lib.pkv_append_attention_layers.argtypes = [ctypes.POINTER(_Cache), i32, P, P, P, i32, P, P,
                                                 P, i32, P, P, i32, i32, i32, ctypes.c_float, i32,
                                                 i32, i32, P, sz, P, sz, P]
+    lib.pkv_hbm_read_probe.argtypes = [P, sz, P, i64, i32, P, P]
     lib.pkv_validate_step.argtypes = [P, i32, P, P, i32, i32, i64, i32, P, i32, i32, i32,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     for name in EXPORTED:
@@ -408,3 +413,18 @@ def validate_step(block_tables, context_lens, query_start_loc, num_decode_seqs: 
     if rc not in (PKV_OK, PKV_ERR_CONTRACT):
         raise PkvError(rc, "pkv_validate_step")
     return int(what.value), int(idx.value)
+
+
+def hbm_read_probe(base, tile_ids, tile_bytes: int, sink, stream=None):
+    """pkv_hbm_read_probe: read tiles tile_ids (int32 device tensor) of `base`
+    (uint8 device tensor) once each, in that order; `sink` is a uint32-sized
+    (int32) device tensor of PROBE_SINK_WORDS words.  Measurement only."""
+    import torch
+    _need(base, torch.uint8, "base")
+    _need(tile_ids, torch.int32, "tile_ids")
+    _need(sink, torch.int32, "sink")
+    if sink.numel() < PROBE_SINK_WORDS:
+        raise ValueError("sink must hold PROBE_SINK_WORDS words")
+    rc = lib.pkv_hbm_read_probe(_ptr(base), base.numel(), _ptr(tile_ids), tile_ids.numel(),
+                                int(tile_bytes), _ptr(sink), _stream(stream))
+    _check(rc, "pkv_hbm_read_probe")

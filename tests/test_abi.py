@@ -162,6 +162,17 @@ def test_layers_plans_are_checked_before_any_launch():
     assert rc == pkv.PKV_ERR_WORKSPACE
 
 
+def test_hbm_read_probe_argument_errors():
+    lib = pkv.lib
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 3000, FAKE, None) == -1   # not 2^k
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 512, FAKE, None) == -1    # < 1 KiB
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, -1, 4096, FAKE, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 0, 4096, FAKE, None) == pkv.PKV_OK
+    assert lib.pkv_hbm_read_probe(None, 1 << 20, FAKE, 4, 4096, FAKE, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, None, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 2048, FAKE, 4, 4096, FAKE, None) == -1     # buffer < tile
+
+
 def test_decode_schedule_size_and_argument_errors():
     # d = 128 steps get a schedule; d = 256 keeps the partition grid
     assert pkv.decode_schedule_size(83, 2, 128, 4352) > 0
