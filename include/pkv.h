@@ -360,6 +360,44 @@ int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,
                                 void* stream);
 
 /*
+ * Bytes of the device scratch array behind pkv_append_attention_step_noalloc
+ * (one copy per GPU the library runs on, held until the process ends).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * pkv_append_attention_step without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc.  The split-KV and prefill partials go
+ * to a scratch array of PKV_NOALLOC_SCRATCH_BYTES inside the library's
+ * device code instead of a caller-owned workspace; the kernels, the result
+ * and every other argument are those of pkv_append_attention_step.  The
+ * call allocates nothing.
+ *
+ *   all arguments   as for pkv_append_attention_step, without workspace and
+ *                   workspace_bytes; the scratch of the current device is
+ *                   used, so `stream` must belong to the current device.
+ * Limit: a step whose pkv_attention_workspace_size (same hints) exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES is refused with PKV_ERR_WORKSPACE before any HIP
+ * call.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's partials: calls in stream order are safe, calls that overlap
+ * on one GPU (other streams, other host threads) race.  The first call on a
+ * device looks up that device's copy of the array; a failure there returns
+ * PKV_ERR_HIP (pkv_last_hip_error names it).
+ * Errors: as for pkv_append_attention_step.
+ */
+int pkv_append_attention_step_noalloc(const pkv_kv_cache* cache, const void* k_new,
+                                      const void* v_new, const int64_t* slot_mapping,
+                                      int32_t num_tokens, const void* q, void* out,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens,
+                                      const int32_t* query_start_loc, int32_t num_seqs,
+                                      int32_t num_decode_seqs, int32_t num_q_heads, float scale,
+                                      int32_t max_context_len, int32_t max_query_len,
+                                      int32_t kv_partition_tokens, const void* schedule,
+                                      size_t schedule_bytes, void* stream);
+
+/*
  * Work-groups of pkv_hbm_read_probe: the sink holds one word per work-group.
  */
 #define PKV_PROBE_SINK_WORDS 2048

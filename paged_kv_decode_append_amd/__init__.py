@@ -6,7 +6,7 @@ the C ABI in include/pkv.h without the ``pkv_`` prefix:
 
     slot_mapping, kv_append, attention_workspace_size, decode_schedule_size,
     decode_schedule, paged_attention_step, append_attention_step,
-    validate_step, hbm_read_probe, status_string,
+    append_attention_step_noalloc, validate_step, hbm_read_probe, status_string,
     last_hip_error, version
 
 There is no fallback: importing this package without a built libpkv.so
@@ -34,11 +34,14 @@ EXPORTED = (
     "pkv_version", "pkv_status_string", "pkv_last_hip_error", "pkv_slot_mapping", "pkv_kv_append",
     "pkv_attention_workspace_size", "pkv_decode_schedule_size", "pkv_decode_schedule",
     "pkv_paged_attention_step", "pkv_append_attention_step", "pkv_append_attention_layers",
-    "pkv_validate_step", "pkv_hbm_read_probe",
+    "pkv_append_attention_step_noalloc", "pkv_validate_step", "pkv_hbm_read_probe",
 )
 
 # work-groups of pkv_hbm_read_probe (words of its sink)
 PROBE_SINK_WORDS = 2048
+
+# bytes of the device scratch behind pkv_append_attention_step_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class PkvError(RuntimeError):
@@ -91,6 +94,9 @@ def _load():
     lib.pkv_append_attention_step.argtypes = [ctypes.POINTER(_Cache), P, P, P, i32, P, P, P, i32,
                                               P, P, i32, i32, i32, ctypes.c_float, i32, i32, i32,
                                               P, sz, P, sz, P]
+    lib.pkv_append_attention_step_noalloc.argtypes = [
+        ctypes.POINTER(_Cache), P, P, P, i32, P, P, P, i32, P, P, i32, i32, i32, ctypes.c_float,
+        i32, i32, i32, P, sz, P]
     lib.pkv_append_attention_layers.argtypes = [ctypes.POINTER(_Cache), i32, P, P, P, i32, P, P,
                                                 P, i32, P, P, i32, i32, i32, ctypes.c_float, i32,
                                                 i32, i32, P, sz, P, sz, P]
@@ -338,6 +344,39 @@ def append_attention_step(cache: KVCache, k_new, v_new, slot_mapping_t, q, out, 
         int(max_context_len), int(max_query_len), int(kv_partition_tokens),
         *_schedule_args(schedule), _ptr(workspace), ws_bytes, _stream(stream))
     _check(rc, "pkv_append_attention_step")
+    return out
+
+
+def append_attention_step_noalloc(cache: KVCache, k_new, v_new, slot_mapping_t, q, out,
+                                  block_tables, context_lens, query_start_loc,
+                                  num_decode_seqs: int, scale: float, max_context_len: int,
+                                  max_query_len: int, kv_partition_tokens: int = 0, stream=None,
+                                  schedule=None):
+    """pkv_append_attention_step_noalloc: append_attention_step with the
+    partials in the library's own device scratch (no workspace argument; the
+    call allocates nothing)."""
+    import torch
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (q, "q"), (out, "out")):
+        _need(t, torch.float16, name)
+    _need(slot_mapping_t, torch.int64, "slot_mapping")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if query_start_loc is not None:
+        _need(query_start_loc, torch.int32, "query_start_loc")
+    T = k_new.shape[0]
+    if v_new.shape != k_new.shape or k_new.shape[1:] != (cache.num_kv_heads, cache.head_dim):
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    if out.shape != q.shape or q.dim() != 3 or q.shape[0] != T or q.shape[2] != cache.head_dim:
+        raise ValueError("q and out must be [T, num_q_heads, head_dim]")
+    if slot_mapping_t.numel() < T:
+        raise ValueError("slot_mapping shorter than the token count")
+    rc = lib.pkv_append_attention_step_noalloc(
+        ctypes.byref(cache._c), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping_t), T, _ptr(q),
+        _ptr(out), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(query_start_loc), context_lens.shape[0], num_decode_seqs, q.shape[1], float(scale),
+        int(max_context_len), int(max_query_len), int(kv_partition_tokens),
+        *_schedule_args(schedule), _stream(stream))
+    _check(rc, "pkv_append_attention_step_noalloc")
     return out
 
 

@@ -162,6 +162,38 @@ def test_layers_plans_are_checked_before_any_launch():
     assert rc == pkv.PKV_ERR_WORKSPACE
 
 
+def _noalloc(cache, kn=FAKE, T=4, nseq=4, ndec=4, hq=12, mcl=1024, maxblk=64, mql=1, qsl=None):
+    return pkv.lib.pkv_append_attention_step_noalloc(
+        ctypes.byref(cache), kn, FAKE, FAKE, T, FAKE, FAKE, FAKE, maxblk, FAKE, qsl, nseq, ndec,
+        hq, 0.1, mcl, mql, 0, None, 0, None)
+
+
+def test_noalloc_step_argument_errors_and_scratch_limit():
+    """The no-allocation step checks its arguments as the workspace step
+    does, and refuses a step whose partials exceed the scratch array before
+    any HIP call (no GPU here: a HIP call would give PKV_ERR_HIP)."""
+    c = _cache()
+    assert pkv.lib.pkv_append_attention_step_noalloc(
+        None, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, 64, FAKE, None, 4, 4, 12, 0.1, 1024, 1, 0,
+        None, 0, None) == -1
+    assert _noalloc(c, kn=None) == -1
+    assert _noalloc(c, hq=18) == -2
+    assert _noalloc(c, nseq=0, ndec=0, T=0) == pkv.PKV_OK
+    # 4,096 decode sequences of up to 262,144 tokens at d = 256: far more
+    # partials than the scratch holds
+    big = _cache(head_dim=256, kv_heads=4)
+    need = pkv.attention_workspace_size(4096, 4096, 16, 4, 256, 262144, 1)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(big, T=4096, nseq=4096, ndec=4096, hq=16, mcl=262144, maxblk=16384) == \
+        pkv.PKV_ERR_WORKSPACE
+    # every benchmark workload's step fits
+    for make in workloads.WORKLOADS.values():
+        wl = make()
+        assert pkv.attention_workspace_size(wl.num_seqs, wl.num_decode_seqs, wl.num_q_heads,
+                                            wl.num_kv_heads, wl.head_dim, wl.max_context_len,
+                                            wl.max_query_len) <= pkv.NOALLOC_SCRATCH_BYTES
+
+
 def test_hbm_read_probe_argument_errors():
     lib = pkv.lib
     assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 3000, FAKE, None) == -1   # not 2^k
