@@ -52,11 +52,11 @@ int check_step_shape(int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_he
   return PKV_OK;
 }
 
-// Workspace: decode partials first, then prefill partials (256-byte aligned).
-size_t prefill_offset(const pkv::DecodePlan& d) { return (d.partial_bytes + 255) / 256 * 256; }
-
+// Workspace: the decode partials and then, over the same bytes, the prefill
+// partials -- the decode kernel and its merge are done with theirs (stream
+// order) before the prefill kernel writes.
 size_t workspace_layout(const pkv::DecodePlan& d, const pkv::PrefillPlan& p) {
-  return p.partial_bytes > 0 ? prefill_offset(d) + p.partial_bytes : d.partial_bytes;
+  return std::max(d.partial_bytes, p.partial_bytes);
 }
 
 thread_local hipError_t t_last_hip_error = hipSuccess;
@@ -238,7 +238,7 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
   const size_t need = workspace_layout(plan, pplan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   if (check_only) return PKV_OK;
-  void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + prefill_offset(plan) : nullptr;
+  void* prefill_ws = need > 0 ? workspace : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
     // quantized cache (partition grid only): with the append, the prefill

@@ -147,18 +147,19 @@ def test_layers_argument_errors_are_found_before_any_launch():
 
 def test_layers_plans_are_checked_before_any_launch():
     """A later layer whose plan needs more workspace than the call brings
-    (d = 256 beside a d = 128 layer, 4 KV heads each) is refused before the
-    first layer is launched: PKV_ERR_WORKSPACE, not the launch error a
-    first layer enqueued without a GPU would give."""
-    small, big = _cache(head_dim=128, kv_heads=4), _cache(head_dim=256, kv_heads=4)
-    need_small = pkv.attention_workspace_size(4, 4, 16, 4, 128, 65536, 1)
-    need_big = pkv.attention_workspace_size(4, 4, 16, 4, 256, 65536, 1)
-    assert need_big > need_small > 0
-    arr = (pkv._Cache * 2)(small, big)
+    (another head_dim, 4 KV heads each) is refused before the first layer
+    is launched: PKV_ERR_WORKSPACE, not the launch error a first layer
+    enqueued without a GPU would give."""
+    a, b = _cache(head_dim=128, kv_heads=4), _cache(head_dim=256, kv_heads=4)
+    need_a = pkv.attention_workspace_size(4, 4, 16, 4, 128, 65536, 1)
+    need_b = pkv.attention_workspace_size(4, 4, 16, 4, 256, 65536, 1)
+    assert need_a != need_b and min(need_a, need_b) > 0
+    first, second = (a, b) if need_a < need_b else (b, a)
+    arr = (pkv._Cache * 2)(first, second)
     ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
     rc = pkv.lib.pkv_append_attention_layers(arr, 2, ptrs, ptrs, FAKE, 4, ptrs, ptrs, FAKE, 4096,
                                              FAKE, None, 4, 4, 16, 0.1, 65536, 1, 0, None, 0,
-                                             FAKE, need_small, None)
+                                             FAKE, min(need_a, need_b), None)
     assert rc == pkv.PKV_ERR_WORKSPACE
 
 
