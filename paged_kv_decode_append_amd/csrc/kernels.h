@@ -106,6 +106,7 @@ hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_po
 struct PrefillPlan {
   int32_t splits;
   bool packed;             // every chunk's G x n rows fit one tile (short chunks)
+  bool wide;               // long chunks at head_dim 128: 32 rows per wave (prefill_wide.hip)
   int32_t split_tiles;     // KV tiles per split (packed; 0: even ranges of the context)
   int64_t max_row_heads;   // bound on (prefill rows x query heads)
   size_t partial_bytes;
@@ -114,6 +115,17 @@ struct PrefillPlan {
 PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t max_context_len, int32_t max_query_len,
                          int32_t kv_partition_tokens);
+
+// The long-chunk kernels at head_dim 128 (prefill_wide.hip): 32 query rows
+// per wave; the partials and their merge are the 16-row kernel's.
+hipError_t launch_prefill_wide(const void* q, const void* k_pool, const void* v_pool,
+                               const float* k_scale, const float* v_scale, int64_t num_blocks,
+                               int32_t num_kv_heads, int32_t num_q_heads,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, const int32_t* query_start_loc,
+                               int32_t first_seq, int32_t num_prefill_seqs,
+                               int32_t max_query_len, float scale, int32_t splits, void* out,
+                               float* part_o, float* part_ml, hipStream_t stream);
 
 // Causal attention of the prefill chunks (sequences first_seq ..
 // first_seq + num_prefill_seqs - 1) on the matrix cores.  With k_scale set

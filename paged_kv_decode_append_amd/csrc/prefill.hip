@@ -56,6 +56,10 @@ constexpr int64_t kGroupsPerCU256 = 2;
 constexpr uint32_t kXcds = 8;
 constexpr int64_t kMaxPrefillSplits = 16;
 constexpr int64_t kPackedRounds = 2;  // packed rows: target rounds of resident work-groups
+// long-chunk kernels at d = 128: 128 rows per work-group and two per CU
+// (fp8 cache), or 256 and one (fp16 cache) -- the same rows per CU
+constexpr int64_t kWideRows = 128;
+constexpr int64_t kWideGroupsPerCU = 2;
 constexpr float kRescaleSlack = 8.f;  // lazy max (base 2): rescale only past m + 8
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -597,6 +601,16 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
                             (kv_tiles + kMaxPrefillSplits - 1) / kMaxPrefillSplits);
     plan.splits = (int32_t)((kv_tiles + per - 1) / per);
     plan.split_tiles = plan.splits > 1 ? (int32_t)per : 0;
+  } else if (head_dim == 128) {
+    // long chunks at d = 128 (prefill_wide.hip): splits for one round of
+    // resident work-groups, counted in 128-row groups, two per CU
+    plan.wide = true;
+    const int64_t wide_groups =
+        (int64_t)num_prefill_seqs * ((max_query_len + kWideRows - 1) / kWideRows) * num_q_heads;
+    int64_t splits = kCUs * kWideGroupsPerCU / wide_groups;
+    splits = std::min<int64_t>(std::min<int64_t>(splits, kMaxPrefillSplits), kv_tiles);
+    plan.splits = (int32_t)std::max<int64_t>(splits, 1);
+    plan.split_tiles = 0;
   } else {
     // as many splits as fit in one round of resident work-groups (no tail round)
     int64_t splits = resident / groups;
@@ -623,6 +637,20 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
       (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
   float* part_o = static_cast<float*>(workspace);
   float* part_ml = part_o ? part_o + (size_t)plan.max_row_heads * plan.splits * D : nullptr;
+  hipError_t err;
+  if (plan.wide) {
+    err = launch_prefill_wide(q, k_pool, v_pool, k_scale, v_scale, num_blocks, num_kv_heads,
+                              num_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                              query_start_loc, first_seq, num_prefill_seqs, max_query_len, scale,
+                              plan.splits, out, part_o, part_ml, stream);
+    if (err != hipSuccess || plan.splits == 1) return err;
+    const int64_t waves = plan.max_row_heads;
+    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0,
+                       stream, part_o, part_ml, query_start_loc, first_seq,
+                       first_seq + num_prefill_seqs, num_q_heads, plan.splits,
+                       plan.max_row_heads, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   if (plan.packed) {
     // x = split, y = KV head: each work-group holds all heads of its group
@@ -649,7 +677,7 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                        scale * kLog2e,
                        static_cast<uint16_t*>(out), part_o, part_ml);
   }
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return err;
   const int64_t waves = plan.max_row_heads;
   hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0,

@@ -49,6 +49,18 @@ def test_qwen_mixed_full_size():
     _report("qwen_mixed layer 5 (64 decodes, all 512 chunk rows)", errs)
 
 
+def test_long_chunk_over_long_context_splits_past_staged_pages():
+    """A 2,048-row chunk over a 20,000-token context: 2 splits of ~157 KV
+    tiles each, so the kernel's pages past the first 256 of a split take
+    their pool offsets from the block table directly (not from the copy
+    staged in LDS).  Sampled rows across the row tiles, checked each as the
+    query that attends positions [0, its position]."""
+    wl = workloads.custom("long_split", [20000], [2048], 0, 12, 2, 128, seed=71)
+    rows = [0, 1, 127, 128, 255, 256, 1000, 1023, 1024, 1791, 2046, 2047]
+    _, _, errs = run_layer_and_check(wl, seq_subset=[], row_samples={0: rows}, poison=False)
+    _report("2,048-row chunk over 20,000 tokens (sampled rows)", errs)
+
+
 def test_fused_chunk_append_matches_separate_calls_with_odd_slots():
     """A step with chunks, some of whose rows are skipped (slot -1: the
     pool's current row is attended) and one written to a slot outside its
