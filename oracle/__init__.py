@@ -24,17 +24,30 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names another build of oracle.c (e.g. with sanitizers).
+_LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile oracle.c with gcc into liboracle.so (plain -O2, no fast-math)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", _LIB_PATH, "-lm"]
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH,
+          sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so (plain -O2, no fast-math).
+
+    src / out: another source (a test's mutated copy) or output path.
+    sanitize: build with clang's AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang, so that the process holds one sanitizer runtime with the
+    library's sanitized host code; load it with that runtime preloaded)."""
+    if sanitize:
+        cmd = [os.environ.get("SAN_CC", "/opt/rocm/llvm/bin/clang"), "-O1", "-g",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+               "-fno-omit-frame-pointer", "-shared-libsan", "-std=c11", "-fopenmp", "-fPIC",
+               "-shared", src, "-o", out, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", src, "-o", out, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    return _LIB_PATH
+    return out
 
 
 def _load():

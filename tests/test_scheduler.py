@@ -1,6 +1,9 @@
 """The host block manager and per-pass scheduler (libpkv.so, include/pkv_sched.h)
 against the plain-Python model in oracle/scheduler.py and the rules of
-deepconcepts.dev, "Continuous Batching Is Not a Bigger Batch".  CPU only."""
+deepconcepts.dev, "Continuous Batching Is Not a Bigger Batch".  The tests of
+the page's rules (102 blocks, the newest preempted, no admission after a
+preemption, max-num-seqs a ceiling, the budget cap) run against both the C++
+and the model.  CPU only."""
 import ctypes
 
 import numpy as np
@@ -44,6 +47,56 @@ def _validate(plan, num_blocks):
     assert rc == pkv.PKV_OK, (bad_what.value, bad_idx.value)
 
 
+class _ModelAsScheduler:
+    """oracle/scheduler.py behind the C++ binding's interface, so that the
+    page-rule tests below pin the model directly as well as the C++."""
+
+    class _Plan:
+        def __init__(self, d):
+            for key in ("num_decode_seqs", "num_preempted", "num_admitted", "recomputed_tokens",
+                        "prefix_hit_tokens"):
+                setattr(self, key, d[key])
+            self.request_ids = np.array(d["request_ids"], dtype=np.int64)
+            self.context_lens = np.array(d["context_lens"], dtype=np.int32)
+            self.new_tokens = np.array(d["new_tokens"], dtype=np.int32)
+            self.num_seqs = len(d["request_ids"])
+
+    def __init__(self, num_blocks, max_num_seqs, budget, width, free_order=None):
+        self.m = model.SchedulerModel(num_blocks, max_num_seqs, budget, width,
+                                      free_order=free_order)
+
+    def add_request(self, rid, prompt, max_new, prefix_id=-1, prefix_len=0):
+        self.m.add_request(rid, prompt, max_new, prefix_id, prefix_len)
+
+    def schedule(self):
+        return self._Plan(self.m.schedule())
+
+    def complete(self):
+        self.m.complete()
+
+    def done(self):
+        return self.m.done()
+
+    def request_blocks(self, rid):
+        r = next((r for r in self.m.running if r.rid == rid), None)
+        return None if r is None or not r.blocks else np.array(r.blocks)
+
+    def stats(self):
+        st = self.m.stats
+        return {"preemptions": st["preemptions"], "generated_tokens": st["generated_tokens"],
+                "peak_running": st["peak_running"], "num_running": len(self.m.running),
+                "free_blocks": len(self.m.free), "num_finished": st["finished"]}
+
+
+IMPLS = ["cpp", "model"]
+
+
+def _make(impl, num_blocks, max_seqs, budget, width=WIDTH, free_order=None):
+    if impl == "cpp":
+        return Scheduler(num_blocks, max_seqs, budget, width, free_order=free_order)
+    return _ModelAsScheduler(num_blocks, max_seqs, budget, width, free_order=free_order)
+
+
 def _run_both(cpp, ref, num_blocks, max_passes=100000, on_plan=None):
     passes = 0
     while not ref.done():
@@ -74,10 +127,11 @@ def _run_both(cpp, ref, num_blocks, max_passes=100000, on_plan=None):
     return st, passes
 
 
-def test_worked_example_holds_102_blocks():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_worked_example_holds_102_blocks(impl):
     """[CB] "Where the batch size actually comes from": a 1,368-token prompt
     that generates 256 tokens ends up holding 102 blocks of 16."""
-    cpp = Scheduler(7281, 256, 8192, WIDTH)
+    cpp = _make(impl, 7281, 256, 8192)
     cpp.add_request(0, 1368, 256)
     most = 0
     while not cpp.done():
@@ -129,7 +183,8 @@ def test_prefix_sharing_matches_the_model_and_never_appends_into_shared_blocks()
     assert st["prefix_hit_tokens"] > 0
 
 
-def test_newest_is_preempted_and_recomputes_from_zero():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_newest_is_preempted_and_recomputes_from_zero(impl):
     """A 12-block pool, three 63-token prompts.  Pass 0 admits request 0
     (63 tokens, 4 blocks) and 1 token of request 1; pass 1 gives request 1
     its other 62 tokens (4 blocks) and admits 1 token of request 2; in pass
@@ -137,7 +192,7 @@ def test_newest_is_preempted_and_recomputes_from_zero():
     request 2, the newest -- here the requester itself -- is preempted, its
     blocks freed, nobody admitted.  It comes back first, recomputing its
     whole prompt from zero."""
-    cpp = Scheduler(12, 8, 64, WIDTH)
+    cpp = _make(impl, 12, 8, 64)
     for rid in range(3):
         cpp.add_request(rid, 63, 40)
     cpp.add_request(3, 16, 4)
@@ -163,9 +218,10 @@ def test_newest_is_preempted_and_recomputes_from_zero():
     assert cpp.stats()["free_blocks"] == 12
 
 
-def test_no_admission_in_any_pass_that_preempted():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_no_admission_in_any_pass_that_preempted(impl):
     prompts, outputs, _ = workloads.serving_requests(num_requests=128)
-    cpp = Scheduler(2000, 256, 4096, WIDTH, free_order=workloads.free_block_order(2000))
+    cpp = _make(impl, 2000, 256, 4096, free_order=workloads.free_block_order(2000))
     for k, (p, o) in enumerate(zip(prompts, outputs)):
         cpp.add_request(k, int(p), int(o))
     preempting = 0
@@ -178,7 +234,8 @@ def test_no_admission_in_any_pass_that_preempted():
     assert preempting > 0
 
 
-def test_max_num_seqs_is_only_a_ceiling():
+@pytest.mark.parametrize("impl", IMPLS)
+def test_max_num_seqs_is_only_a_ceiling(impl):
     """With the page's 16 GiB pool the cache binds before 256 slots do; a
     smaller cap binds instead and removes the preemptions ([CB] introduction:
     max-num-seqs 256 peaks at 83 with preemptions, 64 has none -- the page's
@@ -186,7 +243,7 @@ def test_max_num_seqs_is_only_a_ceiling():
     prompts, outputs, _ = workloads.serving_requests(num_requests=256)
     peaks = {}
     for cap in (256, 64):
-        cpp = Scheduler(7281, cap, 8192, WIDTH, free_order=workloads.free_block_order(7281))
+        cpp = _make(impl, 7281, cap, 8192, free_order=workloads.free_block_order(7281))
         for k, (p, o) in enumerate(zip(prompts, outputs)):
             cpp.add_request(k, int(p), int(o))
         while not cpp.done():
@@ -200,8 +257,9 @@ def test_max_num_seqs_is_only_a_ceiling():
     assert peaks[64]["preemptions"] < peaks[256]["preemptions"]
 
 
-def test_chunked_prefill_caps_new_tokens_by_the_budget():
-    cpp = Scheduler(500, 8, 100, WIDTH)
+@pytest.mark.parametrize("impl", IMPLS)
+def test_chunked_prefill_caps_new_tokens_by_the_budget(impl):
+    cpp = _make(impl, 500, 8, 100)
     cpp.add_request(0, 350, 2)
     sizes = []
     while not cpp.done():
