@@ -156,30 +156,26 @@ def read_probe_rate(tile_bytes: int, bytes_per_launch: int, seed: int = 0):
     """GB/s that pkv_hbm_read_probe sustains reading `bytes_per_launch` per
     launch as whole `tile_bytes` tiles in a random order, from a buffer of at
     least 4 GiB (far beyond the last-level cache), successive launches taking
-    the next tiles of one permutation.  HIP events on the launch stream."""
+    the next tiles of one permutation; 10 launches back to back from one
+    library call, HIP events on the launch stream."""
     import torch
     import paged_kv_decode_append_amd as pkv
     n = max(1, bytes_per_launch // tile_bytes)
+    launches, warm = 10, 2
+    # every launch reads tiles no earlier launch read: together they stay
+    # within one permutation of a buffer of >= 4 GiB when it is large enough
     ntiles = max(n, (4 << 30) // tile_bytes)
     base = torch.zeros(ntiles * tile_bytes, dtype=torch.uint8, device="cuda")
     perm = np.random.default_rng(seed).permutation(ntiles).astype(np.int32)
-    ids = torch.from_numpy(np.concatenate([perm, perm[:n]])).cuda()
+    reps = -(-(launches + warm) * n // ntiles)
+    ids = torch.from_numpy(np.tile(perm, reps)[: (launches + warm) * n].copy()).cuda()
     sink = torch.empty(pkv.PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    launches = 10
-    start = 0
-
-    def launch():
-        nonlocal start
-        pkv.hbm_read_probe(base, ids[start:start + n], tile_bytes, sink)
-        start = (start + n) % ntiles
-
-    for _ in range(2):
-        launch()
+    # the launches of one call run back to back (no host cost between them)
+    pkv.hbm_read_probe(base, ids[: warm * n], tile_bytes, sink, launches=warm)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
-    for _ in range(launches):
-        launch()
+    pkv.hbm_read_probe(base, ids[warm * n:], tile_bytes, sink, launches=launches)
     b.record(stream)
     torch.cuda.synchronize()
     t = a.elapsed_time(b) * 1e-3 / launches

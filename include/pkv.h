@@ -400,31 +400,35 @@ int pkv_append_attention_step_noalloc(const pkv_kv_cache* cache, const void* k_n
 /*
  * Work-groups of pkv_hbm_read_probe: the sink holds one word per work-group.
  */
-#define PKV_PROBE_SINK_WORDS 2048
+#define PKV_PROBE_SINK_WORDS 4096
 
 /*
- * HBM read-rate probe (measurement only; not part of a step).  Reads tiles
- * tile_ids[0 .. num_tiles-1] of `base` (tile t = bytes [t * tile_bytes,
- * (t + 1) * tile_bytes)) once each, in the listed order, and folds the words
- * it read into `sink`, one word per work-group.  With the block size of one
+ * HBM read-rate probe (measurement only; not part of a step).  Runs
+ * `launches` launches back to back on `stream`; launch k reads tiles
+ * tile_ids[k * num_tiles .. (k + 1) * num_tiles - 1] of `base` (tile t =
+ * bytes [t * tile_bytes, (t + 1) * tile_bytes)) once each, in the listed
+ * order, and folds the words it read into `sink`, one word per work-group.  With the block size of one
  * KV head as tile_bytes (4 KiB at head_dim 128, 8 KiB at 256) and the ids in
  * a random order over a buffer much larger than the last-level cache, it is
  * the paged decode's access pattern without its arithmetic: timed around
- * the launch, it gives the read rate HBM sustains for that pattern, the
+ * the launches, it gives the read rate HBM sustains for that pattern at
+ * that launch size (each launch pays its own ramp and drain), the
  * measured denominator beside the 8 TB/s specification (danielfleming.xyz,
  * "Static batching", section "Where scaling stops, and why the prediction
  * missed": read rates reported as a share of peak).
  *
  *   base, base_bytes   device buffer (any content), >= tile_bytes
- *   tile_ids           device int32 [num_tiles]; ids outside
+ *   tile_ids           device int32 [launches * num_tiles]; ids outside
  *                      [0, base_bytes / tile_bytes) are clamped into it
  *   tile_bytes         a power of two in [1024, 65536]
+ *   launches           0 .. 4096
  *   sink               device uint32 [PKV_PROBE_SINK_WORDS], overwritten
  * Asynchronous on `stream`.  Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
  * PKV_ERR_HIP.
  */
 int pkv_hbm_read_probe(const void* base, size_t base_bytes, const int32_t* tile_ids,
-                       int64_t num_tiles, int32_t tile_bytes, uint32_t* sink, void* stream);
+                       int64_t num_tiles, int32_t tile_bytes, int32_t launches, uint32_t* sink,
+                       void* stream);
 
 /*
  * Debug validator (host, synchronous, no GPU): checks on host copies of

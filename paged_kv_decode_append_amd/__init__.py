@@ -40,7 +40,7 @@ EXPORTED = (
 )
 
 # work-groups of pkv_hbm_read_probe (words of its sink)
-PROBE_SINK_WORDS = 2048
+PROBE_SINK_WORDS = 4096
 
 # bytes of the device scratch behind pkv_append_attention_step_noalloc
 NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -102,7 +102,7 @@ def _load():
     lib.pkv_append_attention_layers.argtypes = [ctypes.POINTER(_Cache), i32, P, P, P, i32, P, P,
                                                 P, i32, P, P, i32, i32, i32, ctypes.c_float, i32,
                                                 i32, i32, P, sz, P, sz, P]
-    lib.pkv_hbm_read_probe.argtypes = [P, sz, P, i64, i32, P, P]
+    lib.pkv_hbm_read_probe.argtypes = [P, sz, P, i64, i32, i32, P, P]
     lib.pkv_validate_step.argtypes = [P, i32, P, P, i32, i32, i64, i32, P, i32, i32, i32,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     for name in EXPORTED:
@@ -456,16 +456,21 @@ def validate_step(block_tables, context_lens, query_start_loc, num_decode_seqs: 
     return int(what.value), int(idx.value)
 
 
-def hbm_read_probe(base, tile_ids, tile_bytes: int, sink, stream=None):
-    """pkv_hbm_read_probe: read tiles tile_ids (int32 device tensor) of `base`
-    (uint8 device tensor) once each, in that order; `sink` is a uint32-sized
-    (int32) device tensor of PROBE_SINK_WORDS words.  Measurement only."""
+def hbm_read_probe(base, tile_ids, tile_bytes: int, sink, launches: int = 1, stream=None):
+    """pkv_hbm_read_probe: `launches` launches back to back, launch k reading
+    tiles tile_ids[k n .. (k + 1) n) (int32 device tensor, n = its length /
+    launches) of `base` (uint8 device tensor) once each, in that order; `sink`
+    is a uint32-sized (int32) device tensor of PROBE_SINK_WORDS words.
+    Measurement only."""
     import torch
     _need(base, torch.uint8, "base")
     _need(tile_ids, torch.int32, "tile_ids")
     _need(sink, torch.int32, "sink")
     if sink.numel() < PROBE_SINK_WORDS:
         raise ValueError("sink must hold PROBE_SINK_WORDS words")
-    rc = lib.pkv_hbm_read_probe(_ptr(base), base.numel(), _ptr(tile_ids), tile_ids.numel(),
-                                int(tile_bytes), _ptr(sink), _stream(stream))
+    if launches < 1 or tile_ids.numel() % launches:
+        raise ValueError("tile_ids must hold launches equal windows")
+    rc = lib.pkv_hbm_read_probe(_ptr(base), base.numel(), _ptr(tile_ids),
+                                tile_ids.numel() // launches, int(tile_bytes), int(launches),
+                                _ptr(sink), _stream(stream))
     _check(rc, "pkv_hbm_read_probe")

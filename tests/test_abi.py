@@ -197,13 +197,17 @@ def test_noalloc_step_argument_errors_and_scratch_limit():
 
 def test_hbm_read_probe_argument_errors():
     lib = pkv.lib
-    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 3000, FAKE, None) == -1   # not 2^k
-    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 512, FAKE, None) == -1    # < 1 KiB
-    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, -1, 4096, FAKE, None) == -1
-    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 0, 4096, FAKE, None) == pkv.PKV_OK
-    assert lib.pkv_hbm_read_probe(None, 1 << 20, FAKE, 4, 4096, FAKE, None) == -1
-    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, None, None) == -1
-    assert lib.pkv_hbm_read_probe(FAKE, 2048, FAKE, 4, 4096, FAKE, None) == -1     # buffer < tile
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 3000, 1, FAKE, None) == -1   # not 2^k
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 512, 1, FAKE, None) == -1    # < 1 KiB
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, -1, 4096, 1, FAKE, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, -1, FAKE, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 0, 4096, 1, FAKE, None) == pkv.PKV_OK
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, 0, FAKE, None) == pkv.PKV_OK
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, 4097, FAKE, None) == \
+        pkv.PKV_ERR_UNSUPPORTED
+    assert lib.pkv_hbm_read_probe(None, 1 << 20, FAKE, 4, 4096, 1, FAKE, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 1 << 20, FAKE, 4, 4096, 1, None, None) == -1
+    assert lib.pkv_hbm_read_probe(FAKE, 2048, FAKE, 4, 4096, 1, FAKE, None) == -1     # buffer < tile
 
 
 def test_decode_schedule_size_and_argument_errors():
