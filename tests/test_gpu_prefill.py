@@ -49,6 +49,19 @@ def test_qwen_mixed_full_size():
     _report("qwen_mixed layer 5 (64 decodes, all 512 chunk rows)", errs)
 
 
+@pytest.mark.parametrize("hq,hkv", [(12, 2), (8, 8), (16, 2)])
+def test_chunks_of_several_row_tiles_over_short_contexts(hq, hkv):
+    """Chunks of 257 .. 700 rows (two or three 256-row tiles of the d = 128
+    kernel) with little or no cached prefix: splits of one or two 64-token
+    tiles, empty splits, and the loads' tail waits from the first step on;
+    every row checked."""
+    ctx = [1, 600, 700, 257, 520]
+    new = [1, 600, 520, 257, 513]
+    wl = workloads.custom("row_tiles", ctx, new, 1, hq, hkv, 128, seed=hq + 17 * hkv)
+    _, _, errs = run_layer_and_check(wl)
+    _report(f"several row tiles G={hq // hkv}", errs)
+
+
 def test_long_chunk_over_long_context_splits_past_staged_pages():
     """A 2,048-row chunk over a 20,000-token context: 2 splits of ~157 KV
     tiles each, so the kernel's pages past the first 256 of a split take
