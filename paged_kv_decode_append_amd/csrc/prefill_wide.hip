@@ -555,10 +555,22 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
     const uint32_t id = (uint32_t)bt_row[pg];
     return (int64_t)(id < (uint64_t)num_blocks ? id : num_blocks - 1) * block_stride + head_off;
   };
+  // Q^T fragments (B operands): row my_row, d = 16 c + 8 lgrp .. +7; loaded
+  // beside the block-table reads, both waited for by the barrier below
+  // (later waits count only the tile loads)
+  f16x8 qb[kD / 16];
+  {
+    const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + head) * kD;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c)
+      qb[c] = *reinterpret_cast<const f16x8*>(qrow + 16 * c + 8 * lgrp);
+  }
   const int pg_begin = kt_begin * (KT / 16);
   const int pg_end = min(kt_end * (KT / 16) - 1, last_pg) + 1;
   for (int e = tid; e < kIdPages; e += 64 * kDmaWaves)
     if (pg_begin + e < pg_end) s_page[e] = block_off(pg_begin + e);
+#pragma unroll
+  for (int c = 0; c < kD / 16; ++c) asm volatile("" ::"v"(qb[c]));  // Q in before the barrier
   __syncthreads();
 
   // Wave w loads half of page w % 4 of a tile (tokens 16 (w % 4) + 8 (w / 4)
@@ -580,14 +592,6 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
     }
   };
 
-  // Q^T fragments (B operands): row my_row, d = 16 c + 8 lgrp .. +7
-  f16x8 qb[kD / 16];
-  {
-    const uint16_t* qrow = q + ((int64_t)(row_base + my_row) * num_q_heads + head) * kD;
-#pragma unroll
-    for (int c = 0; c < kD / 16; ++c)
-      qb[c] = *reinterpret_cast<const f16x8*>(qrow + 16 * c + 8 * lgrp);
-  }
   f32x16 o[kD / 32];
 #pragma unroll
   for (int dt = 0; dt < kD / 32; ++dt)
@@ -642,18 +646,32 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
     return scl;
   };
 
-  // Prologue: K(kt_begin) landed; then, in the order the steps would have
-  // issued them, K(kt_begin + 1 + a) and V(kt_begin + a) for a < kAhead
-  // loading; the scores of tile kt_begin computed.
+  // Prologue: K(kt_begin), then, in the order the steps would have issued
+  // them, K(kt_begin + 1 + a) and V(kt_begin + a) for a < kAhead, all issued
+  // at once; K(kt_begin) waited for (the later loads stay in flight: the
+  // first step's K(kt_begin + 1) arrives with it) and its scores computed.
   dma_tile(k_pool, k_lds0, kt_begin, false);
-  wait_all_loads();
-  __syncthreads();
   if (kt_begin + 1 < kt_end) dma_tile(k_pool, k_lds1, kt_begin + 1, false);
   dma_tile(v_pool, v_lds0, kt_begin, true);
   if (kt_begin + 2 < kt_end) dma_tile(k_pool, k_lds2, kt_begin + 2, false);
   if (kt_begin + 1 < kt_end) dma_tile(v_pool, v_lds1, kt_begin + 1, true);
   if (kt_begin + 3 < kt_end) dma_tile(k_pool, k_lds3, kt_begin + 3, false);
   if (kt_begin + 2 < kt_end) dma_tile(v_pool, v_lds2, kt_begin + 2, true);
+  {
+    // this wave's loads issued after K(kt_begin): 2 per tile
+    static_assert(kLoadsPerTile == 4, "2 loads per wave and tile of K, 2 of V");
+    const int later = 2 * (1 + 2 * (kt_begin + 1 < kt_end) + 2 * (kt_begin + 2 < kt_end) +
+                           (kt_begin + 3 < kt_end));
+    if (later >= 12)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | 12);
+    else if (later >= 10)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | 10);
+    else if (later >= 6)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | 6);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | 2);
+  }
+  lds_barrier();  // every wave's share of K(kt_begin) landed
   f32x16 s[2];
   if (wave_live) {
 #pragma unroll
