@@ -75,10 +75,11 @@ def test_short_chunks_of_up_to_32_rows(hq, hkv, qmax, fused):
     _report(f"short chunks G={hq // hkv} n<={qmax} fused={fused}", errs)
 
 
-@pytest.mark.parametrize("part", [64, 128, 256, 1024])
+@pytest.mark.parametrize("part", [64, 128, 256, 1024, 4096])
 def test_short_chunk_splits(part):
     """The same with the context cut into fixed splits (some empty for the
-    short contexts), merged by log-sum-exp."""
+    short contexts), merged by log-sum-exp; 4096: each context (up to 4,096
+    tokens) in one split, no merge."""
     ctx = [1, 16, 100, 700, 1500, 3000, 4096]
     new = [1, 4, 4, 3, 4, 2, 4]
     wl = workloads.custom("short_chunk_splits", ctx, new, 0, 12, 2, 128, seed=part)
