@@ -56,8 +56,8 @@ constexpr int64_t kGroupsPerCU256 = 2;
 constexpr uint32_t kXcds = 8;
 constexpr int64_t kMaxPrefillSplits = 16;
 constexpr int64_t kPackedRounds = 2;  // packed rows: target rounds of resident work-groups
-// long-chunk kernels at d = 128: 128 rows per work-group and two per CU
-// (fp8 cache), or 256 and one (fp16 cache) -- the same rows per CU
+// long-chunk kernels at d = 128 (fp16 and fp8 caches): 256 rows per
+// work-group, one per CU, counted in 128-row groups, two per CU
 constexpr int64_t kWideRows = 128;
 constexpr int64_t kWideGroupsPerCU = 2;
 constexpr float kRescaleSlack = 8.f;  // lazy max (base 2): rescale only past m + 8
