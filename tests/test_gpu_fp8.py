@@ -236,6 +236,49 @@ def test_qwen_mixed_full_size_fp8():
     _report("qwen_mixed fp8 layer 5 (64 decodes, all 512 chunk rows)", errs)
 
 
+@pytest.mark.parametrize("hq,hkv", [(12, 2), (8, 8), (16, 2)])
+def test_fp8_chunks_of_several_row_tiles_over_short_contexts(hq, hkv):
+    """Chunks of 257 .. 700 rows (two or three 256-row tiles of the d = 128
+    kernel) with little or no cached prefix over an fp8 cache: splits of one
+    or two 64-token tiles, empty splits, the prologue's and the last steps'
+    load counts, and the tiles converted from codes in the first step; every
+    row checked."""
+    ctx = [1, 600, 700, 257, 520]
+    new = [1, 600, 520, 257, 513]
+    wl = workloads.custom("fp8_row_tiles", ctx, new, 1, hq, hkv, 128, seed=hq + 19 * hkv)
+    t = _fp8_cache(wl)
+    t0 = {n: _np(t[n]) for n in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, fused=True)
+    kc, vc, ks, vs, qsl = _append_ref(wl, t0, t)
+    ref = oracle.paged_attention_fp8(host_bits(t["q"]), kc, vc, ks, vs, wl.block_tables,
+                                     wl.context_lens, qsl, wl.scale)
+    errs = assert_close(out.cpu().numpy(), ref, f"fp8 several row tiles G={hq // hkv}")
+    _report(f"fp8 several row tiles G={hq // hkv}", errs)
+
+
+def test_fp8_long_chunk_over_long_context_splits_past_staged_pages():
+    """A 2,048-row chunk over a 20,000-token context over an fp8 cache: 2
+    splits of ~157 KV tiles each, so the codes and row scales of pages past
+    the first 256 of a split come by pool offsets read from the block table
+    directly.  Sampled rows across the row tiles, each checked as the query
+    that attends positions [0, its position] of the appended cache."""
+    n, ctx = 2048, 20000
+    wl = workloads.custom("fp8_long_split", [ctx], [n], 0, 12, 2, 128, seed=73)
+    t = _fp8_cache(wl, poison=False)
+    t0 = {k: _np(t[k]) for k in ("k_codes", "v_codes", "k_scale", "v_scale")}
+    _, out = _run(wl, t, fused=True)
+    kc, vc, ks, vs, _ = _append_ref(wl, t0, t)
+    q = host_bits(t["q"])
+    got = out.cpu().numpy()
+    worst = (0.0, 0.0)
+    for r in [0, 1, 127, 128, 255, 256, 1000, 1023, 1024, 1791, 2046, 2047]:
+        ref = oracle.paged_attention_fp8(q[r:r + 1], kc, vc, ks, vs, wl.block_tables[:1],
+                                         np.array([ctx - n + r + 1], np.int32), None, wl.scale)
+        e = assert_close(got[r:r + 1], ref, f"fp8 long chunk row {r}")
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    _report("fp8 2,048-row chunk over 20,000 tokens (sampled rows)", worst)
+
+
 @pytest.mark.parametrize("kind", ["decode", "short", "long"])
 def test_row_scales_spanning_a_wide_range(kind):
     """K row scales from 2^-11 to 2^7 move the logits over many orders of
