@@ -57,6 +57,46 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// v_permlane32_swap: lanes 32..63 of a trade places with lanes 0..31 of b;
+// v_permlane16_swap: rows 1 and 3 of a (16 lanes each) with rows 0 and 2 of
+// b.  Inline asm: hipcc's builtins for them lose one of the two results when
+// both operands hold the same value.  The s_nop gives the two wait states the
+// swaps need after a VALU write of their operands.
+__device__ __forceinline__ void permlane32_swap(uint32_t& a, uint32_t& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(uint32_t& a, uint32_t& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// The maximum / sum of this lane's value and lane l ^ 32's, the same bits in
+// both lanes (the halves exchanged in registers, no LDS round trip; the sum
+// adds the lower lane's value first).
+__device__ __forceinline__ float max_of_halves(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);  // a: lane l % 32's value, b: lane 32 + l % 32's
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float sum_of_halves(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane32_swap(a, b);
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// The maximum / sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the wave's four
+// 16-lane rows), the same bits in all four: rows 0-1 and 2-3 are paired
+// first, then the halves; the sum is (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ float max_of_rows(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);  // a: the even row's value, b: the odd row's
+  return max_of_halves(fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b)));
+}
+__device__ __forceinline__ float sum_of_rows(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  permlane16_swap(a, b);
+  return sum_of_halves(__builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+}
+
 // Keeps the compiler from moving LDS accesses across this point (no instruction).
 __device__ __forceinline__ void wave_fence() { __builtin_amdgcn_wave_barrier(); }
 

@@ -379,8 +379,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
         vmax = fmaxf(fmaxf(vmax, fmaxf(vs.x, vs.y)), fmaxf(vs.z, vs.w));
       }
       // lanes of one lgrp hold the same tokens; the four groups cover the tile
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+      vmax = max_of_rows(vmax);
       if (vmax != vref) {  // the same in every lane and wave
         const float ratio = vref / vmax;  // exact: powers of two (0 before the first tile)
 #pragma unroll
@@ -431,8 +430,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
           for (int e = 0; e < 4; ++e) ext = fminf(ext, s[hh][t][e]);
       }
       float tile_max = ext * sc;
-      tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 16));
-      tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+      tile_max = max_of_rows(tile_max);
       // Lazy max: the reference only moves when a score passes it by more
       // than kRescaleSlack (weights stay <= 2^8, exact in fp16 range), so
       // after the first tiles the O rescale is skipped by the whole wave.
@@ -482,8 +480,7 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    l_row[hh] += __shfl_xor(l_row[hh], 16);
-    l_row[hh] += __shfl_xor(l_row[hh], 32);
+    l_row[hh] = sum_of_rows(l_row[hh]);
   }
   if (!row_valid) return;
   const int64_t first_row = query_start_loc[first_seq];

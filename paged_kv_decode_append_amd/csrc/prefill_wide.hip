@@ -265,7 +265,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) ext = fmaxf(ext, sc[st][r]);
     float tile_max = ext * scl;
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+    tile_max = max_of_halves(tile_max);
     if (__any(tile_max > m_row + kRescaleSlack)) {
       const float m_new = tile_max > m_row + kRescaleSlack ? tile_max : m_row;
       const float alpha = m_new == -__builtin_huge_valf() ? 1.f : fast_exp2(m_row - m_new);
@@ -303,17 +303,17 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
       __builtin_amdgcn_s_waitcnt(kWaitVm0 | 2);
   }
   lds_barrier();  // every wave's share of K(kt_begin) landed
-  f32x16 s[2];
+  f32x16 s0[2], s1[2];  // scores of the current and next tile, alternating
   if (wave_live) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s0[st][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < kD / 16; ++c) {
       const unsigned char* p = k_lds0 + (k_xor ^ (32u * c));
-      s[0] = mfma32(*reinterpret_cast<const f16x8*>(p), qb[c], s[0]);
-      s[1] = mfma32(*reinterpret_cast<const f16x8*>(p + 32 * kRowBytes), qb[c], s[1]);
+      s0[0] = mfma32(*reinterpret_cast<const f16x8*>(p), qb[c], s0[0]);
+      s0[1] = mfma32(*reinterpret_cast<const f16x8*>(p + 32 * kRowBytes), qb[c], s0[1]);
     }
   }
 
@@ -327,8 +327,8 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
   // then the 16 products of the O update, their transposing reads issued
   // ahead.  The matrix cores work on the next scores while the VALU turns
   // this tile's scores into weights.
-  auto step = [&](int kt, const unsigned char* kn, unsigned char* kc, const unsigned char* vc,
-                  unsigned char* vn) {
+  auto step = [&](int kt, f32x16 (&s)[2], f32x16 (&sn)[2], const unsigned char* kn,
+                  unsigned char* kc, const unsigned char* vc, unsigned char* vn) {
     // this wave's share of K(kt + 1) and V(kt): all but the two later steps'
     // loads (fewer were issued near the end: then wait for all)
     if (kt + kAhead < kt_end)
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
     const float scl = softmax_max(s, kt);
     const float neg_ref = m_row == -__builtin_huge_valf() ? 0.f : -m_row;
 
-    f32x16 sn[2];  // the next tile's scores (past the last tile: a stale buffer's, unused)
+    // sn: the next tile's scores (past the last tile: a stale buffer's, unused)
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -411,17 +411,15 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) s[st] = sn[st];
   };
   for (int kt = kt_begin; kt < kt_end; kt += kStages) {
-    step(kt, k_lds1, k_lds0, v_lds0, v_lds3);
-    if (kt + 1 < kt_end) step(kt + 1, k_lds2, k_lds1, v_lds1, v_lds0);
-    if (kt + 2 < kt_end) step(kt + 2, k_lds3, k_lds2, v_lds2, v_lds1);
-    if (kt + 3 < kt_end) step(kt + 3, k_lds0, k_lds3, v_lds3, v_lds2);
+    step(kt, s0, s1, k_lds1, k_lds0, v_lds0, v_lds3);
+    if (kt + 1 < kt_end) step(kt + 1, s1, s0, k_lds2, k_lds1, v_lds1, v_lds0);
+    if (kt + 2 < kt_end) step(kt + 2, s0, s1, k_lds3, k_lds2, v_lds2, v_lds1);
+    if (kt + 3 < kt_end) step(kt + 3, s1, s0, k_lds0, k_lds3, v_lds3, v_lds2);
   }
 
-  l_row += __shfl_xor(l_row, 32);
+  l_row = sum_of_halves(l_row);
   if (!row_valid) return;
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
   const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + head;
@@ -668,7 +666,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma8_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) ext = fmaxf(ext, sc[st][r]);
     float tile_max = ext * scl;
-    tile_max = fmaxf(tile_max, __shfl_xor(tile_max, 32));
+    tile_max = max_of_halves(tile_max);
     if (__any(tile_max > m_row + kRescaleSlack)) {
       const float m_new = tile_max > m_row + kRescaleSlack ? tile_max : m_row;
       const float alpha = m_new == -__builtin_huge_valf() ? 1.f : fast_exp2(m_row - m_new);
@@ -720,17 +718,17 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma8_kernel(
   convert_tile(vc_lds0, vs_lds[0], v16_lds0, true);
   if (kt_begin + 1 < kt_end) convert_tile(kc_lds1, ks_lds[1], k16_lds1, false);
   lds_barrier();
-  f32x16 s[2];
+  f32x16 s0[2], s1[2];  // scores of the current and next tile, alternating
   if (wave_live) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s0[st][r] = 0.f;
 #pragma unroll
     for (int c = 0; c < kD / 16; ++c) {
       const unsigned char* p = k16_lds0 + (k_xor ^ (32u * c));
-      s[0] = mfma32(*reinterpret_cast<const f16x8*>(p), qb[c], s[0]);
-      s[1] = mfma32(*reinterpret_cast<const f16x8*>(p + 32 * kRowBytes), qb[c], s[1]);
+      s0[0] = mfma32(*reinterpret_cast<const f16x8*>(p), qb[c], s0[0]);
+      s0[1] = mfma32(*reinterpret_cast<const f16x8*>(p + 32 * kRowBytes), qb[c], s0[1]);
     }
   }
 
@@ -739,7 +737,8 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma8_kernel(
   // (kt + 4) to kdst / ksdst, V codes and scales (kt + 3) to vdst / vsdst;
   // converts K(kt + 2) (kcin, scales kcs -> kconv) and V(kt + 1) (vcin,
   // scales vcs -> vconv).
-  auto step = [&](int kt, const unsigned char* kn, const unsigned char* vcur,
+  auto step = [&](int kt, f32x16 (&s)[2], f32x16 (&sn)[2], const unsigned char* kn,
+                  const unsigned char* vcur,
                   unsigned char* kdst, float* ksdst, unsigned char* vdst, float* vsdst,
                   const unsigned char* kcin, const float* kcs, unsigned char* kconv,
                   const unsigned char* vcin, const float* vcs, unsigned char* vconv) {
@@ -767,7 +766,7 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma8_kernel(
     const float scl = softmax_max(s, kt);
     const float neg_ref = m_row == -__builtin_huge_valf() ? 0.f : -m_row;
 
-    f32x16 sn[2];  // the next tile's scores (past the last tile: a stale buffer's, unused)
+    // sn: the next tile's scores (past the last tile: a stale buffer's, unused)
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -835,27 +834,25 @@ __global__ __launch_bounds__(64 * kDmaWaves) void prefill_wide_dma8_kernel(
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     convert_next();
-#pragma unroll
-    for (int st = 0; st < 2; ++st) s[st] = sn[st];
   };
   // slots for r = kt - kt_begin: codes (K kt + 4 -> r % 4; V kt + 3 ->
   // (r + 3) % 4), scales (tile t -> (t - kt_begin) % 4), fp16 (K kt + 1 ->
   // (r + 1) % 2; V kt -> r % 2; K kt + 2 -> r % 2; V kt + 1 -> (r + 1) % 2)
   for (int kt = kt_begin; kt < kt_end; kt += 4) {
-    step(kt, k16_lds1, v16_lds0, kc_lds0, ks_lds[0], vc_lds3, vs_lds[3], kc_lds2, ks_lds[2],
+    step(kt, s0, s1, k16_lds1, v16_lds0, kc_lds0, ks_lds[0], vc_lds3, vs_lds[3], kc_lds2, ks_lds[2],
          k16_lds0, vc_lds1, vs_lds[1], v16_lds1);
     if (kt + 1 < kt_end)
-      step(kt + 1, k16_lds0, v16_lds1, kc_lds1, ks_lds[1], vc_lds0, vs_lds[0], kc_lds3,
+      step(kt + 1, s1, s0, k16_lds0, v16_lds1, kc_lds1, ks_lds[1], vc_lds0, vs_lds[0], kc_lds3,
            ks_lds[3], k16_lds1, vc_lds2, vs_lds[2], v16_lds0);
     if (kt + 2 < kt_end)
-      step(kt + 2, k16_lds1, v16_lds0, kc_lds2, ks_lds[2], vc_lds1, vs_lds[1], kc_lds0,
+      step(kt + 2, s0, s1, k16_lds1, v16_lds0, kc_lds2, ks_lds[2], vc_lds1, vs_lds[1], kc_lds0,
            ks_lds[0], k16_lds0, vc_lds3, vs_lds[3], v16_lds1);
     if (kt + 3 < kt_end)
-      step(kt + 3, k16_lds0, v16_lds1, kc_lds3, ks_lds[3], vc_lds2, vs_lds[2], kc_lds1,
+      step(kt + 3, s1, s0, k16_lds0, v16_lds1, kc_lds3, ks_lds[3], vc_lds2, vs_lds[2], kc_lds1,
            ks_lds[1], k16_lds1, vc_lds0, vs_lds[0], v16_lds0);
   }
 
-  l_row += __shfl_xor(l_row, 32);
+  l_row = sum_of_halves(l_row);
   if (!row_valid) return;
   const float inv = l_row > 0.f ? 2.f / l_row : 0.f;  // O was in units of 2 (V tiles hold V / 2)
   const int64_t row_head = (int64_t)(row_base + my_row) * num_q_heads + head;
