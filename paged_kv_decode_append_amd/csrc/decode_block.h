@@ -161,14 +161,17 @@ template <int D>
 __device__ __forceinline__ void load_v(KVRegs<D>& r, __amdgpu_buffer_rsrc_t vtile, int lane) {
   if constexpr (D == 128) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      r.v[e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             vtile, ((4 * (lane >> 4) + e) * D + 8 * (lane & 15)) * 2, 0, 0));
+    for (int e = 0; e < 4; ++e) {
+      const int off = ((4 * (lane >> 4) + e) * D + 8 * (lane & 15)) * 2;
+      r.v[e] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(vtile, off, 0, kLoadNonTemporal));
+    }
   } else {
     const int base = (D / 64) * lane * 2;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
-      r.v[t] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vtile, base + t * D * 2, 0, 0));
+      r.v[t] = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(vtile, base + t * D * 2, 0, kLoadNonTemporal));
   }
 }
 

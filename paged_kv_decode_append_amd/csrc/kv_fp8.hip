@@ -204,11 +204,11 @@ __device__ __forceinline__ void load8(KV8Regs<D>& r, const Block8Rsrc& t, int la
   for (int e = 0; e < 4; ++e) {
     const int off = (4 * grp + e) * D + VB * row;
     if constexpr (VB == 8) {
-      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(t.v, off, 0, 0));
+      const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(t.v, off, 0, kLoadNonTemporal));
       r.v[e][0] = x.x;
       r.v[e][1] = x.y;
     } else {
-      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t.v, off, 0, 0));
+      const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(t.v, off, 0, kLoadNonTemporal));
       r.v[e][0] = x.x;
       r.v[e][1] = x.y;
       r.v[e][2] = x.z;
