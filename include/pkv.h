@@ -289,8 +289,12 @@ int pkv_paged_attention_step(const pkv_kv_cache* cache, const void* q, void* out
  * decode kernel itself: the work-group that reads the block holding
  * position ctx_i - 1 takes the new row from k_new / v_new instead of the
  * pool and writes it to slot_mapping[i] at its end.  Prefill tokens (rows
- * num_decode_seqs .. num_tokens-1) are appended by the append kernel before
- * the prefill kernel runs.  Over an fp8 cache both quantize the rows as
+ * num_decode_seqs .. num_tokens-1) are appended by extra work-groups of the
+ * same decode launch (by the append kernel when num_decode_seqs is 0), before
+ * the prefill kernel runs.  Since the decode work-groups read the pools
+ * meanwhile, a new token's slot must lie in a block that no other sequence's
+ * context lists, as the block manager of pkv_sched.h hands them out
+ * (pkv_validate_step code 10).  Over an fp8 cache both quantize the rows as
  * pkv_kv_append does.
  *
  *   k_new, v_new   device fp16 [num_tokens][num_kv_heads][head_dim]
@@ -447,6 +451,9 @@ int pkv_hbm_read_probe(const void* base, size_t base_bytes, const int32_t* tile_
  *   8  max_context_len or max_query_len smaller than an actual length
  *   9  a non-negative slot that is not the table's slot of its token's
  *      position (ctx_i - n_i + k)
+ *  10  a non-negative slot in a block that another sequence's context also
+ *      lists (shared blocks are read-only: new tokens go to blocks that
+ *      belong to one sequence)
  */
 int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
                       const int32_t* context_lens, const int32_t* query_start_loc,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -188,9 +189,10 @@ namespace {
 
 // Attention of one layer; with k_new non-null the new tokens' append is done
 // here too: the decode tokens' inside the decode kernel, the prefill tokens'
-// by the append kernel ahead of the prefill kernel.  With check_only, every
-// check (arguments, plans, workspace and schedule sizes, grid limits) runs
-// and nothing is launched.
+// by extra work-groups of the decode launch (by the append kernel when the
+// step has no decode sequence), both ahead of the prefill kernel.  With
+// check_only, every check (arguments, plans, workspace and schedule sizes,
+// grid limits) runs and nothing is launched.
 int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new,
                    const void* v_new,
                    const int64_t* slot_mapping, int32_t num_tokens, const void* q, void* out,
@@ -221,7 +223,11 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
   if (num_prefill > kMaxGridYZ || num_q_heads > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
   pkv::DecodePlan plan = pkv::plan_decode(num_decode_seqs, cache->num_kv_heads, num_q_heads,
                                           cache->head_dim, max_context_len, kv_partition_tokens);
-  if (plan.max_parts > kMaxGridYZ) return PKV_ERR_UNSUPPORTED;
+  // with the append, a step with decode sequences appends the prefill rows
+  // in work-groups of the decode launch: up to append_groups more z slices
+  const bool rows_in_decode = fused && num_decode_seqs > 0 && num_tokens > num_decode_seqs;
+  const int32_t extra_z = rows_in_decode ? pkv::append_groups(num_tokens - num_decode_seqs) : 0;
+  if (plan.max_parts > kMaxGridYZ - extra_z) return PKV_ERR_UNSUPPORTED;
   const pkv::DecodeSchedulePlan splan = pkv::plan_decode_schedule(
       num_decode_seqs, cache->num_kv_heads, num_q_heads, cache->head_dim, max_context_len);
   // The balanced schedule replaces the partition grid whenever the latter
@@ -246,7 +252,7 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
     // the decode kernel quantizes and appends the decode rows itself
     float* k_scale = static_cast<float*>(cache->k_scale);
     float* v_scale = static_cast<float*>(cache->v_scale);
-    if (fused && num_tokens > num_decode_seqs) {
+    if (fused && num_tokens > num_decode_seqs && !rows_in_decode) {
       const size_t row_bytes = (size_t)cache->num_kv_heads * cache->head_dim * 2;
       rc = from_hip(pkv::launch_kv_append_fp8(
           cache->k_pool, cache->v_pool, k_scale, v_scale, cache->num_blocks,
@@ -256,7 +262,8 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
           slot_mapping + num_decode_seqs, num_tokens - num_decode_seqs, s));
       if (rc != PKV_OK) return rc;
     }
-    const pkv::DecodeAppend app8{k_new, v_new, fused ? slot_mapping : nullptr};
+    const pkv::DecodeAppend app8{k_new, v_new, fused ? slot_mapping : nullptr,
+                                 fused ? num_tokens : 0};
     rc = from_hip(pkv::launch_paged_decode_fp8(
         q, cache->k_pool, cache->v_pool, k_scale, v_scale, cache->num_blocks,
         cache->num_kv_heads, num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq,
@@ -269,7 +276,7 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
                                         num_prefill, max_query_len, scale, pplan, out,
                                         prefill_ws, s));
   }
-  if (fused && num_tokens > num_decode_seqs) {
+  if (fused && num_tokens > num_decode_seqs && !rows_in_decode) {
     // rows of the prefill chunks follow the decode rows
     const size_t row_bytes = (size_t)cache->num_kv_heads * cache->head_dim * 2;
     rc = from_hip(pkv::launch_kv_append(
@@ -279,7 +286,8 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
         slot_mapping + num_decode_seqs, num_tokens - num_decode_seqs, s));
     if (rc != PKV_OK) return rc;
   }
-  const pkv::DecodeAppend app{k_new, v_new, fused ? slot_mapping : nullptr};
+  const pkv::DecodeAppend app{k_new, v_new, fused ? slot_mapping : nullptr,
+                             fused ? num_tokens : 0};
   if (scheduled)
     rc = from_hip(pkv::launch_paged_decode_scheduled(
         q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
@@ -430,6 +438,22 @@ int pkv_validate_step(const int32_t* block_tables, int32_t max_blocks_per_seq,
         const int64_t b = block_tables[(int64_t)i * max_blocks_per_seq + p / block_size];
         if (s != b * block_size + p % block_size) return fail(9, first + k);
       }
+    }
+    // a block that receives a new token is listed by no other sequence's
+    // context (the fused step appends while other work-groups read)
+    std::unordered_map<int64_t, int32_t> owner;
+    std::unordered_set<int64_t> shared;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int64_t used = ((int64_t)context_lens[i] + block_size - 1) / block_size;
+      for (int64_t j = 0; j < used; ++j) {
+        const int64_t b = block_tables[(int64_t)i * max_blocks_per_seq + j];
+        const auto it = owner.emplace(b, i).first;
+        if (it->second != i) shared.insert(b);
+      }
+    }
+    for (int32_t t = 0; t < num_tokens; ++t) {
+      const int64_t s = slot_mapping[t];
+      if (s >= 0 && shared.count(s / block_size)) return fail(10, t);
     }
   }
   return PKV_OK;

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping,
+    int32_t num_tokens) {
   constexpr int GP = (G + 3) & ~3;
   // d = 128: two blocks (16 KiB) in flight per wave by refilling a buffer as
   // soon as each half is consumed; d = 256: one block is already 16 KiB, and
@@ -90,6 +91,15 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
   __shared__ __attribute__((aligned(16))) uint16_t s_new[APPEND ? 2 * D : 8];  // K row, V row
 
+  if (APPEND && (int)blockIdx.z >= max_parts) {
+    // the z slices past the partitions (dispatched last): prefill rows
+    const int64_t nxy = (int64_t)gridDim.x * gridDim.y;
+    decode_block::append_rows<D>(k_pool, v_pool, num_blocks, num_kv_heads, k_new, v_new,
+                                 slot_mapping, gridDim.x, num_tokens,
+                                 (blockIdx.z - max_parts) * nxy + blockIdx.y * gridDim.x + blockIdx.x,
+                                 (gridDim.z - max_parts) * nxy, (int)threadIdx.x, 64 * kWaves);
+    return;
+  }
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
@@ -412,15 +422,21 @@ hipError_t launch_decode_dga(const void* q, void* k_pool, void* v_pool, int64_t 
   float* part_o = static_cast<float*>(workspace);
   float* part_ml =
       part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
+  // prefill rows of the step (rows past the decode rows) get z slices of
+  // their own after the partitions
+  const int64_t xy = (int64_t)num_decode_seqs * num_kv_heads;
+  const int32_t app_z =
+      APPEND ? (int32_t)((append_groups(app.num_tokens - num_decode_seqs) + xy - 1) / xy) : 0;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   hipLaunchKernelGGL((paged_decode_kernel<D, G, APPEND>),
-                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
+                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts + app_z), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<uint16_t*>(k_pool),
                      static_cast<uint16_t*>(v_pool), num_blocks, num_kv_heads, block_tables,
                      max_blocks_per_seq, context_lens, ctx_clamp, plan.partition_blocks,
                      plan.max_parts, scale * kLog2e, static_cast<uint16_t*>(out), part_o,
                      part_ml, static_cast<const uint16_t*>(app.k_new),
-                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
+                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping,
+                     app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
   return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,

@@ -357,5 +357,37 @@ __device__ __forceinline__ void block_pv(KVRegs<D>& r, WaveState<D, G>& st, int 
   }
 }
 
+// Prefill rows appended by extra work-groups of a decode launch: rows
+// r_begin .. r_end - 1 of k_new / v_new ([rows][Hkv][D] fp16) go to their
+// slots (slot_mapping[row]; negative, or past the pool: skipped), one 16-byte
+// chunk per thread and pass; work-group w of nw takes every nw-th pass.
+// Their slots lie in blocks that only their own (prefill) sequence lists, so
+// the decode work-groups of the same launch never read them.
+template <int D>
+__device__ __forceinline__ void append_rows(uint16_t* __restrict__ k_pool,
+                                            uint16_t* __restrict__ v_pool, int64_t num_blocks,
+                                            int num_kv_heads, const uint16_t* __restrict__ k_new,
+                                            const uint16_t* __restrict__ v_new,
+                                            const int64_t* __restrict__ slot_mapping,
+                                            int64_t r_begin, int64_t r_end, int64_t w,
+                                            int64_t nw, int tid, int threads) {
+  constexpr int RCH = D / 8;  // 16-byte chunks of one head's row
+  const int per_pool = num_kv_heads * RCH;
+  const int64_t total = (r_end - r_begin) * 2 * per_pool;
+  for (int64_t idx = w * threads + tid; idx < total; idx += nw * threads) {
+    const int64_t t = r_begin + idx / (2 * per_pool);
+    int c = (int)(idx % (2 * per_pool));
+    const bool is_v = c >= per_pool;
+    c -= is_v ? per_pool : 0;
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0 || slot / 16 >= num_blocks) continue;
+    const int g = c / RCH, ch = c - g * RCH;
+    const uint4 val =
+        reinterpret_cast<const uint4*>((is_v ? v_new : k_new) + (t * num_kv_heads + g) * D)[ch];
+    reinterpret_cast<uint4*>((is_v ? v_pool : k_pool) +
+                             (((slot / 16) * num_kv_heads + g) * 16 + slot % 16) * D)[ch] = val;
+  }
+}
+
 }  // namespace decode_block
 }  // namespace pkv

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
     const int32_t* __restrict__ sched, int32_t U, int32_t nwg, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int64_t* __restrict__ slot_mapping) {
+    const int64_t* __restrict__ slot_mapping, int32_t num_decode_seqs, int32_t num_tokens) {
   constexpr int GP = (G + 3) & ~3, RCH = D / 8;
   constexpr bool kEarlyRefill = D == 128;
   constexpr int QCH = G * D / 8;
@@ -241,6 +241,12 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = blockIdx.x;
+  if (APPEND && w >= nwg) {
+    // the work-groups past the schedule's (dispatched last): prefill rows
+    append_rows<D>(k_pool, v_pool, num_blocks, num_kv_heads, k_new, v_new, slot_mapping,
+                   num_decode_seqs, num_tokens, w - nwg, (int)gridDim.x - nwg, tid, 64 * kWaves);
+    return;
+  }
   const int32_t* rec = sched + sched_rec_offset(U) + (int64_t)w * kRecWords;
   // the whole 80-byte record at once (16-byte aligned): head + 4 descriptors
   int4 rv[1 + kInlineSegs];
@@ -717,14 +723,16 @@ hipError_t launch_sched_dga(const void* q, void* k_pool, void* v_pool, int64_t n
   float* part_ml = part_o + (size_t)pieces * G * D;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   const int32_t U = num_decode_seqs * num_kv_heads;
-  hipLaunchKernelGGL((paged_decode_sched_kernel<D, G, APPEND>), dim3(plan.num_groups),
+  const int32_t app_groups = APPEND ? append_groups(app.num_tokens - num_decode_seqs) : 0;
+  hipLaunchKernelGGL((paged_decode_sched_kernel<D, G, APPEND>), dim3(plan.num_groups + app_groups),
                      dim3(64 * kWaves), 0, stream, static_cast<const uint16_t*>(q),
                      static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), num_blocks,
                      num_kv_heads, block_tables, max_blocks_per_seq, sched, U, plan.num_groups,
                      scale * kLog2e,
                      static_cast<uint16_t*>(out), part_o, part_ml,
                      static_cast<const uint16_t*>(app.k_new),
-                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
+                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping, num_decode_seqs,
+                     app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((piece_merge_kernel<D, G>),

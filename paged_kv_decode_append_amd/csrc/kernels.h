@@ -4,6 +4,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -39,7 +41,14 @@ struct DecodeAppend {
   const void* k_new;
   const void* v_new;
   const int64_t* slot_mapping;
+  int32_t num_tokens;  // rows of k_new / v_new: rows past the decode rows (prefill
+                       // chunks' tokens) are appended by extra work-groups
 };
+
+// Work-groups a decode launch adds for appending `rows` prefill rows.
+inline int32_t append_groups(int64_t rows) {
+  return rows <= 0 ? 0 : (int32_t)std::min<int64_t>((rows + 7) / 8, 128);
+}
 
 hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_t num_blocks,
                                int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,

@@ -114,18 +114,16 @@ __device__ __forceinline__ void store_codes(uint8_t* dst, uint32_t c) {
     *reinterpret_cast<uint32_t*>(dst) = c;
 }
 
-// One wave per (token, KV head) row of K (grid.y = 0) or V (grid.y = 1),
-// four rows per work-group; lane l quantizes values EPL*l .. EPL*l + EPL-1.
+// Quantizes row r of K (is_v false) or V of the new tokens ([tokens][Hkv][D]
+// fp16, row r = token r / Hkv, KV head r % Hkv) into its slot: one wave,
+// lane l quantizing values EPL*l .. EPL*l + EPL-1.
 template <int D>
-__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+__device__ __forceinline__ void append_row_fp8(
     uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
     float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int64_t* __restrict__ slot_mapping, int64_t rows) {
+    const int64_t* __restrict__ slot_mapping, int64_t r, bool is_v, int lane) {
   constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
   const int64_t t = r / num_kv_heads;
   const int g = (int)(r - t * num_kv_heads);
   const int64_t slot = slot_mapping[t];
@@ -133,12 +131,25 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(
   const int64_t b = slot / kBlockSize;
   if (b >= num_blocks) return;  // beyond the pool (a broken contract): skipped
   const int o = (int)(slot % kBlockSize);
-  const bool is_v = blockIdx.y == 1;
   int e;
   const uint32_t c = quantize_row_wave<D>((is_v ? v_new : k_new) + r * D, lane, e);
   const int64_t row = ((b * num_kv_heads + g) * kBlockSize + o);
   store_codes<D>((is_v ? v_codes : k_codes) + row * D + EPL * lane, c);
   if (lane == 0) (is_v ? v_scale : k_scale)[row] = exp2i(e);
+}
+
+// One wave per (token, KV head) row of K (grid.y = 0) or V (grid.y = 1),
+// four rows per work-group.
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_fp8_kernel(
+    uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, int64_t num_blocks, int32_t num_kv_heads,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int64_t* __restrict__ slot_mapping, int64_t rows) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  append_row_fp8<D>(k_codes, v_codes, k_scale, v_scale, num_blocks, num_kv_heads, k_new, v_new,
+                    slot_mapping, r, blockIdx.y == 1, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------- decode ---
@@ -407,7 +418,8 @@ __global__ __launch_bounds__(64 * kWaves, D == 128 ? 2 : 1) void paged_decode_fp
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping) {
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slot_mapping,
+    int32_t num_tokens) {
   constexpr int EPL = D / 64;
   // Blocks in flight per wave (4 KiB each at d = 128, 8 KiB at d = 256).
   // Measured on MI355X: at d = 128 two per wave at two waves per SIMD beat
@@ -422,6 +434,19 @@ __global__ __launch_bounds__(64 * kWaves, D == 128 ? 2 : 1) void paged_decode_fp
   __shared__ __attribute__((aligned(16))) uint8_t s_newc[2][APPEND ? D : 16];  // K, V codes
   __shared__ float s_news[2];                                                // their scales
 
+  if (APPEND && (int)blockIdx.z >= max_parts) {
+    // the z slices past the partitions (dispatched last): prefill rows, one
+    // wave per (token, KV head) row of K or V
+    const int64_t nxy = (int64_t)gridDim.x * gridDim.y;
+    const int64_t w = (blockIdx.z - max_parts) * nxy + blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t nw = (gridDim.z - max_parts) * nxy;
+    const int64_t r0 = (int64_t)gridDim.x * num_kv_heads;  // past the decode rows
+    const int64_t n = 2 * ((int64_t)num_tokens * num_kv_heads - r0);
+    for (int64_t k = w * kWaves + (threadIdx.x >> 6); k < n; k += nw * kWaves)
+      append_row_fp8<D>(k_codes, v_codes, k_scale, v_scale, num_blocks, num_kv_heads, k_new,
+                        v_new, slot_mapping, r0 + (k >> 1), (k & 1) != 0, threadIdx.x & 63);
+    return;
+  }
   const int i = blockIdx.x, g = blockIdx.y;
   const int part = max_parts - 1 - (int)blockIdx.z;  // highest partitions dispatch first
   const int num_q_heads = num_kv_heads * G;
@@ -623,16 +648,22 @@ hipError_t launch_decode_fp8_dg(const void* q, void* k_codes, void* v_codes, flo
   float* part_o = static_cast<float*>(workspace);
   float* part_ml =
       part_o ? part_o + (size_t)num_decode_seqs * num_q_heads * plan.max_parts * D : nullptr;
+  // prefill rows of the step (rows past the decode rows) get z slices of
+  // their own after the partitions
+  const int64_t xy = (int64_t)num_decode_seqs * num_kv_heads;
+  const int32_t app_z =
+      APPEND ? (int32_t)((append_groups(app.num_tokens - num_decode_seqs) + xy - 1) / xy) : 0;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   hipLaunchKernelGGL((paged_decode_fp8_kernel<D, G, APPEND>),
-                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts), dim3(64 * kWaves), 0,
+                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts + app_z), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<uint8_t*>(k_codes),
                      static_cast<uint8_t*>(v_codes), k_scale, v_scale, num_blocks,
                      num_kv_heads, block_tables, max_blocks_per_seq, context_lens, ctx_clamp,
                      plan.partition_blocks, plan.max_parts, scale * kLog2e,
                      static_cast<uint16_t*>(out), part_o, part_ml,
                      static_cast<const uint16_t*>(app.k_new),
-                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping);
+                     static_cast<const uint16_t*>(app.v_new), app.slot_mapping,
+                     app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
   return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,

@@ -278,3 +278,9 @@ def test_validator_reports_each_violation():
     assert v(slots=pad) == (0, -1)                       # a skipped token is fine
     moved = good.copy(); moved[2] = wl.free_blocks[0] * 16  # a free slot, not its position's
     assert v(slots=moved) == (9, 2)
+    # a new token's block listed by another sequence's context (read while written)
+    b10 = bt.copy(); b10[0, 0] = bt[1, 3]                # seq 0 now reads seq 1's last block
+    c10 = ctx.copy(); c10[1] = 60                        # seq 1's new token at offset 11, seq 0's at 15
+    assert v(bt=b10, ctx=c10, slots=oracle.slot_mapping(b10, c10, None, 16)) == (10, 0)
+    shared_ro = bt.copy(); shared_ro[1, 0] = bt[2, 0]    # a full block shared, no token written to it
+    assert v(bt=shared_ro, slots=oracle.slot_mapping(shared_ro, ctx, None, 16)) == (0, -1)
