@@ -367,7 +367,7 @@ int pkv_append_attention_layers(const pkv_kv_cache* caches, int32_t num_layers,
  * Bytes of the device scratch array behind pkv_append_attention_step_noalloc
  * (one copy per GPU the library runs on, held until the process ends).
  */
-#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * pkv_append_attention_step without a workspace argument, for callers that

@@ -43,7 +43,7 @@ EXPORTED = (
 PROBE_SINK_WORDS = 4096
 
 # bytes of the device scratch behind pkv_append_attention_step_noalloc
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PkvError(RuntimeError):

@@ -56,8 +56,16 @@ int check_step_shape(int32_t num_seqs, int32_t num_decode_seqs, int32_t num_q_he
 // Workspace: the decode partials and then, over the same bytes, the prefill
 // partials -- the decode kernel and its merge are done with theirs (stream
 // order) before the prefill kernel writes.
+// Workspace of a step: the decode part's partials at its start; the prefill
+// chunks' after them when the step has both, since the decode merge then
+// runs in the step's combined merge after the prefill kernel (otherwise the
+// chunks reuse the same bytes: the decode merge is done before they write).
+size_t chunk_partial_offset(const pkv::DecodePlan& d, const pkv::PrefillPlan& p) {
+  return d.partial_bytes > 0 && p.partial_bytes > 0 ? (d.partial_bytes + 255) / 256 * 256 : 0;
+}
 size_t workspace_layout(const pkv::DecodePlan& d, const pkv::PrefillPlan& p) {
-  return std::max(d.partial_bytes, p.partial_bytes);
+  const size_t off = chunk_partial_offset(d, p);
+  return off > 0 ? off + p.partial_bytes : std::max(d.partial_bytes, p.partial_bytes);
 }
 
 thread_local hipError_t t_last_hip_error = hipSuccess;
@@ -244,7 +252,14 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
   const size_t need = workspace_layout(plan, pplan);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
   if (check_only) return PKV_OK;
-  void* prefill_ws = need > 0 ? workspace : nullptr;
+  void* prefill_ws = need > 0 ? static_cast<char*>(workspace) + chunk_partial_offset(plan, pplan)
+                              : nullptr;
+  // a decode merge is left to the step's combined merge when the chunks are
+  // split too (one launch fewer)
+  pkv::DecodeMerge dm;
+  pkv::DecodeMerge* const defer =
+      num_prefill > 0 && pplan.splits > 1 && chunk_partial_offset(plan, pplan) > 0 ? &dm
+                                                                                   : nullptr;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (cache->kv_dtype == PKV_KV_FP8_E4M3) {
     // quantized cache (partition grid only): with the append, the prefill
@@ -267,14 +282,14 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
     rc = from_hip(pkv::launch_paged_decode_fp8(
         q, cache->k_pool, cache->v_pool, k_scale, v_scale, cache->num_blocks,
         cache->num_kv_heads, num_q_heads, cache->head_dim, block_tables, max_blocks_per_seq,
-        context_lens, num_decode_seqs, scale, plan, app8, out, workspace, s));
+        context_lens, num_decode_seqs, scale, plan, app8, out, workspace, s, defer));
     if (rc != PKV_OK) return rc;
     return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, k_scale, v_scale,
                                         cache->num_blocks, cache->num_kv_heads, num_q_heads,
                                         cache->head_dim, block_tables, max_blocks_per_seq,
                                         context_lens, query_start_loc, num_decode_seqs,
                                         num_prefill, max_query_len, scale, pplan, out,
-                                        prefill_ws, s));
+                                        prefill_ws, s, defer));
   }
   if (fused && num_tokens > num_decode_seqs && !rows_in_decode) {
     // rows of the prefill chunks follow the decode rows
@@ -292,19 +307,19 @@ int attention_step(bool check_only, const pkv_kv_cache* cache, const void* k_new
     rc = from_hip(pkv::launch_paged_decode_scheduled(
         q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
         cache->head_dim, block_tables, max_blocks_per_seq, num_decode_seqs, scale, splan,
-        schedule, app, out, workspace, s));
+        schedule, app, out, workspace, s, defer));
   else
     rc = from_hip(pkv::launch_paged_decode(
         q, cache->k_pool, cache->v_pool, cache->num_blocks, cache->num_kv_heads, num_q_heads,
         cache->head_dim, block_tables, max_blocks_per_seq, context_lens, num_decode_seqs, scale,
-        plan, app, out, workspace, s));
+        plan, app, out, workspace, s, defer));
   if (rc != PKV_OK) return rc;
   return from_hip(pkv::launch_prefill(q, cache->k_pool, cache->v_pool, nullptr, nullptr,
                                       cache->num_blocks, cache->num_kv_heads, num_q_heads,
                                       cache->head_dim, block_tables, max_blocks_per_seq,
                                       context_lens, query_start_loc, num_decode_seqs,
                                       num_prefill, max_query_len, scale, pplan, out,
-                                      prefill_ws, s));
+                                      prefill_ws, s, defer));
 }
 
 }  // namespace

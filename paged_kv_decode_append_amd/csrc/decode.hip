@@ -46,6 +46,7 @@
 #include "decode_block.h"
 #include "device_util.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace pkv {
 
@@ -313,99 +314,14 @@ __global__ __launch_bounds__(64 * kWaves) void paged_decode_kernel(
   }
 }
 
-// One work-group per (sequence, query head) with more than one partition:
-//   M = max_p m_p,  w_p = l_p 2^(m_p - M),  O = sum_p w_p o_p / sum_p w_p.
-// The merge sits between two kernels on the step's critical path, so its
-// memory round trips are what it costs: the context length and the (m, l)
-// pairs are requested together (thread p holds pair p; pairs past the
-// sequence's partition count are stale and selected away), and the first
-// kMergeUnroll partitions of each wave's o vectors (wave w takes every 4th
-// partition from w) are in flight while M is reduced.
-constexpr int kMergeUnroll = 4;
-
+// One work-group per (sequence, query head) with more than one partition.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ context_lens, int32_t ctx_clamp, int32_t partition_blocks,
     int32_t max_parts, int32_t num_q_heads, uint16_t* __restrict__ out) {
-  constexpr int EPL = D / 64;
-  constexpr int kStride = 4 * kMergeUnroll;  // partitions per round of the 4 waves
-  __shared__ float s_max[4];
-  __shared__ float s_w[256];
-  __shared__ float s_wsum[4];
-  __shared__ float s_acc[4][D];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row_head = blockIdx.x;
-  const int i = row_head / num_q_heads;
-  const float* ml = part_ml + (int64_t)row_head * max_parts * 2;
-  const float* po = part_o + (int64_t)row_head * max_parts * D + EPL * lane;
-  const int ctx = context_lens[i];
-  float2 own = {-__builtin_huge_valf(), 0.f};
-  if (tid < max_parts) own = *reinterpret_cast<const float2*>(ml + 2 * tid);
-  const int nblk = (min(ctx, ctx_clamp) + 15) >> 4;
-  const int np = (nblk + partition_blocks - 1) / partition_blocks;
-  if (np <= 1) return;  // written directly by the decode kernel
-
-  // Every partition p < np holds at least one position: m_p is finite,
-  // l_p > 0, o_p written.  Loads of p >= np re-read partition np - 1.
-  float v[kMergeUnroll][EPL];
-#pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) {
-    const int pc = min(wave + 4 * u, np - 1);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)pc * D + e];
-  }
-
-  float M = tid < np ? own.x : -__builtin_huge_valf();
-  for (int p = tid + 256; p < np; p += 256) M = fmaxf(M, ml[2 * p]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) s_max[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-  s_w[tid] = tid < np ? own.y * fast_exp2(own.x - M) : 0.f;
-  __syncthreads();
-  auto weight = [&](int p) -> float {
-    if (p >= np) return 0.f;
-    if (p < 256) return s_w[p];
-    return ml[2 * p + 1] * fast_exp2(ml[2 * p] - M);
-  };
-
-  float W = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) {
-    const float w = weight(wave + 4 * u);
-    W += w;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += w * v[u][e];
-  }
-  // more partitions than one round holds (long contexts)
-  for (int p0 = wave + kStride; p0 < np; p0 += kStride) {
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const int pc = min(p0 + 4 * u, np - 1);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[u][e] = po[(int64_t)pc * D + e];
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeUnroll; ++u) {
-      const float w = weight(p0 + 4 * u);
-      W += w;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += w * v[u][e];
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) s_acc[wave][EPL * lane + e] = acc[e];
-  if (lane == 0) s_wsum[wave] = W;
-  __syncthreads();
-  if (tid < D) {
-    const float total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
-    const float o = s_acc[0][tid] + s_acc[1][tid] + s_acc[2][tid] + s_acc[3][tid];
-    out[(int64_t)row_head * D + tid] = __builtin_bit_cast(uint16_t, (f16)(o / total));
-  }
+  merge::lse_merge_row<D>(part_o, part_ml, context_lens, ctx_clamp, partition_blocks, max_parts,
+                          num_q_heads, out, (int)blockIdx.x);
 }
 
 template <int D, int G, bool APPEND>
@@ -414,7 +330,7 @@ hipError_t launch_decode_dga(const void* q, void* k_pool, void* v_pool, int64_t 
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t num_decode_seqs, float scale, const DecodePlan& plan,
                              const DecodeAppend& app, void* out, void* workspace,
-                             hipStream_t stream) {
+                             hipStream_t stream, DecodeMerge* defer) {
   const int32_t num_q_heads = num_kv_heads * G;
   const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
                                             (int64_t)plan.max_parts * plan.partition_blocks * 16);
@@ -439,6 +355,11 @@ hipError_t launch_decode_dga(const void* q, void* k_pool, void* v_pool, int64_t 
                      app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
+  if (defer) {
+    *defer = grid_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
+                        num_q_heads);
+    return hipSuccess;
+  }
   return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
                              num_q_heads, D, out, stream);
 }
@@ -448,16 +369,16 @@ hipError_t launch_decode_d(int32_t group, const void* q, void* k_pool, void* v_p
                            int64_t num_blocks, int32_t num_kv_heads, const int32_t* bt,
                            int32_t maxblk, const int32_t* ctx, int32_t nseq, float scale,
                            const DecodePlan& plan, const DecodeAppend& app, void* out, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, DecodeMerge* defer) {
   const bool fused = app.k_new != nullptr;
 #define PKV_CASE(GG)                                                                         \
   case GG:                                                                                  \
     return fused ? launch_decode_dga<D, GG, true>(q, k_pool, v_pool, num_blocks,            \
                                                   num_kv_heads, bt, maxblk, ctx, nseq,      \
-                                                  scale, plan, app, out, ws, stream)        \
+                                                  scale, plan, app, out, ws, stream, defer) \
                  : launch_decode_dga<D, GG, false>(q, k_pool, v_pool, num_blocks,           \
                                                    num_kv_heads, bt, maxblk, ctx, nseq,     \
-                                                   scale, plan, app, out, ws, stream);
+                                                   scale, plan, app, out, ws, stream, defer);
   switch (group) {
     PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
     PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
@@ -520,17 +441,17 @@ hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t num_decode_seqs, float scale,
                                const DecodePlan& plan, const DecodeAppend& app, void* out,
-                               void* workspace, hipStream_t stream) {
+                               void* workspace, hipStream_t stream, DecodeMerge* defer) {
   if (num_decode_seqs == 0) return hipSuccess;
   const int32_t group = num_q_heads / num_kv_heads;
   if (head_dim == 128)
     return launch_decode_d<128>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                 block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
-                                scale, plan, app, out, workspace, stream);
+                                scale, plan, app, out, workspace, stream, defer);
   if (head_dim == 256)
     return launch_decode_d<256>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                 block_tables, max_blocks_per_seq, context_lens, num_decode_seqs,
-                                scale, plan, app, out, workspace, stream);
+                                scale, plan, app, out, workspace, stream, defer);
   return hipErrorInvalidValue;
 }
 

@@ -32,48 +32,24 @@
 #include "decode_block.h"
 #include "device_util.h"
 #include "kernels.h"
+#include "merge.h"
+#include "sched_layout.h"
 
 namespace pkv {
 
 namespace {
 
 using namespace decode_block;
+using namespace sched;
 
 constexpr int kWaves = 4;
 constexpr int32_t kSegCost = 2;          // fixed cost of a segment, in blocks
-constexpr int kInlineSegs = 4;           // segment descriptors inside the record
 constexpr int kMaxSegs = 128;            // segments per work-group (host-enforced bound)
 constexpr int kMaxWgBlocks = 2048;       // blocks per work-group (host-enforced bound)
 constexpr int kSchedThreads = 1024;
 constexpr int32_t kMaxSchedUnits = 16384;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Layout of the schedule buffer (int32 words):
-//   [0] W (total cost)  [1] NWG  [2] U  [3] unused
-//   P[U]       inclusive prefix of the unit costs (pad to 4 words)
-//   rec[NWG]   per work-group: int4 head {n, overflow base, 0, 0},
-//              int4 desc[kInlineSegs]
-//   ovf[...]   descriptors k >= kInlineSegs, dense (capacity U + NWG)
-//   um[U]      per unit: int2 {first work-group with a piece, work-groups
-//              spanned} (the merge of split units)
-// A descriptor is {u, jb, je, ctx}: unit u, its blocks [jb, je), context
-// length of u's sequence (clamped).
-constexpr int kRecWords = 4 + 4 * kInlineSegs;
-
-__host__ __device__ inline int64_t sched_p_offset() { return 4; }
-__host__ __device__ inline int64_t sched_rec_offset(int32_t U) { return 4 + (((int64_t)U + 3) & ~3LL); }
-__host__ __device__ inline int64_t sched_ovf_offset(int32_t U, int32_t nwg) {
-  return sched_rec_offset(U) + (int64_t)nwg * kRecWords;
-}
-// Overflow descriptors: at most one per (unit, work-group) piece beyond the
-// inline ones, and pieces number at most U + NWG.
-// Per unit: {first work-group holding a piece, work-groups spanned}.
-__host__ __device__ inline int64_t sched_um_offset(int32_t U, int32_t nwg) {
-  return sched_ovf_offset(U, nwg) + 4 * ((int64_t)U + nwg);
-}
-__host__ __device__ inline int64_t sched_words(int32_t U, int32_t nwg) {
-  return sched_um_offset(U, nwg) + 2 * (int64_t)U;
-}
 
 // Work-group of the block at cost position c (ranges [C_w, C_w+1),
 // C_w = floor(w W / NWG)).
@@ -648,66 +624,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void paged_decode_sched_kernel(
 }
 
 // Merge of the pieces of split units: one 4-wave work-group per (unit, query
-// head of its group); pieces w = wf .. wf + np - 1 at slots u + w (work-groups
-// with an empty cost range hold none).  Each wave merges its pieces in one
-// pass (running log-sum-exp), then the 4 waves combine through LDS.
+// head of its group).
 template <int D, int G>
 __global__ __launch_bounds__(256) void piece_merge_kernel(
     const int32_t* __restrict__ sched, int32_t U, int32_t nwg, int32_t num_kv_heads,
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     uint16_t* __restrict__ out) {
-  constexpr int EPL = D / 64;
-  __shared__ float s_m[4], s_l[4];
-  __shared__ float s_acc[4][D];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int32_t u = blockIdx.x, h = blockIdx.y;
-  if (u >= U) return;
-  const int32_t W = sched[0];
-  const int2 um = reinterpret_cast<const int2*>(sched + sched_um_offset(U, nwg))[u];
-  const int32_t wf = max(0, min(nwg - 1, um.x));
-  const int32_t np = min(um.y, nwg - wf);
-  if (np <= 1 || W <= 0) return;  // whole: written by the decode kernel
-  float M = -__builtin_huge_valf(), L = 0.f, acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p = wave; p < np; p += 4) {
-    const int32_t ww = wf + p;
-    if ((int64_t)(ww + 1) * W / nwg <= (int64_t)ww * W / nwg) continue;  // empty range
-    const int64_t pidx = ((int64_t)u + ww) * G + h;
-    const float mp = part_ml[pidx * 2], lp = part_ml[pidx * 2 + 1];
-    float op[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) op[e] = part_o[pidx * D + EPL * lane + e];
-    if (!(lp > 0.f)) continue;
-    const float Mn = fmaxf(M, mp);
-    const float a = fast_exp2(M - Mn), b = lp * fast_exp2(mp - Mn);
-    L = L * a + b;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = acc[e] * a + b * op[e];
-    M = Mn;
-  }
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) s_acc[wave][EPL * lane + e] = acc[e];
-  if (lane == 0) {
-    s_m[wave] = M;
-    s_l[wave] = L;
-  }
-  __syncthreads();
-  if (tid < D) {
-    const float Mt = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
-    float Lt = 0.f, o = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      if (s_l[ww] > 0.f) {
-        const float a = fast_exp2(s_m[ww] - Mt);
-        Lt += a * s_l[ww];
-        o += a * s_acc[ww][tid];
-      }
-    }
-    const int i = u / num_kv_heads, g = u - i * num_kv_heads;
-    const int64_t row_head = (int64_t)i * num_kv_heads * G + g * G + h;
-    out[row_head * D + tid] = __builtin_bit_cast(uint16_t, (f16)(o / Lt));
-  }
+  merge::piece_merge_unit<D>(sched, U, nwg, num_kv_heads, G, part_o, part_ml, out,
+                             (int32_t)blockIdx.x, (int32_t)blockIdx.y);
 }
 
 template <int D, int G, bool APPEND>
@@ -716,7 +640,7 @@ hipError_t launch_sched_dga(const void* q, void* k_pool, void* v_pool, int64_t n
                             int32_t max_blocks_per_seq, int32_t num_decode_seqs, float scale,
                             const DecodeSchedulePlan& plan, const void* schedule,
                             const DecodeAppend& app, void* out, void* workspace,
-                            hipStream_t stream) {
+                            hipStream_t stream, DecodeMerge* defer) {
   const int32_t* sched = static_cast<const int32_t*>(schedule);
   float* part_o = static_cast<float*>(workspace);
   const int64_t pieces = (int64_t)num_decode_seqs * num_kv_heads + plan.num_groups;
@@ -735,6 +659,20 @@ hipError_t launch_sched_dga(const void* q, void* k_pool, void* v_pool, int64_t n
                      app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (defer) {
+    DecodeMerge m;
+    m.groups = U * G;
+    m.pieces = true;
+    m.part_o = part_o;
+    m.part_ml = part_ml;
+    m.sched = sched;
+    m.units = U;
+    m.sched_groups = plan.num_groups;
+    m.num_kv_heads = num_kv_heads;
+    m.group = G;
+    *defer = m;
+    return hipSuccess;
+  }
   hipLaunchKernelGGL((piece_merge_kernel<D, G>),
                      dim3((uint32_t)U, G), dim3(256), 0, stream, sched, U, plan.num_groups,
                      num_kv_heads, part_o, part_ml, static_cast<uint16_t*>(out));
@@ -746,16 +684,18 @@ hipError_t launch_sched_d(int32_t group, const void* q, void* k_pool, void* v_po
                           int64_t num_blocks, int32_t num_kv_heads, const int32_t* bt,
                           int32_t maxblk, int32_t nseq, float scale,
                           const DecodeSchedulePlan& plan, const void* schedule,
-                          const DecodeAppend& app, void* out, void* ws, hipStream_t stream) {
+                          const DecodeAppend& app, void* out, void* ws, hipStream_t stream,
+                          DecodeMerge* defer) {
   const bool fused = app.k_new != nullptr;
 #define PKV_CASE(GG)                                                                         \
   case GG:                                                                                  \
     return fused ? launch_sched_dga<D, GG, true>(q, k_pool, v_pool, num_blocks, num_kv_heads, \
                                                  bt, maxblk, nseq, scale, plan, schedule,   \
-                                                 app, out, ws, stream)                      \
+                                                 app, out, ws, stream, defer)               \
                  : launch_sched_dga<D, GG, false>(q, k_pool, v_pool, num_blocks,            \
                                                   num_kv_heads, bt, maxblk, nseq, scale,    \
-                                                  plan, schedule, app, out, ws, stream);
+                                                  plan, schedule, app, out, ws, stream,     \
+                                                  defer);
   switch (group) {
     PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
     PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
@@ -812,13 +752,14 @@ hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_po
                                          int32_t max_blocks_per_seq, int32_t num_decode_seqs,
                                          float scale, const DecodeSchedulePlan& plan,
                                          const void* schedule, const DecodeAppend& app,
-                                         void* out, void* workspace, hipStream_t stream) {
+                                         void* out, void* workspace, hipStream_t stream,
+                                         DecodeMerge* defer) {
   if (num_decode_seqs == 0) return hipSuccess;
   const int32_t group = num_q_heads / num_kv_heads;
   if (head_dim == 128)
     return launch_sched_d<128>(group, q, k_pool, v_pool, num_blocks, num_kv_heads,
                                block_tables, max_blocks_per_seq, num_decode_seqs, scale, plan,
-                               schedule, app, out, workspace, stream);
+                               schedule, app, out, workspace, stream, defer);
   return hipErrorInvalidValue;
 }
 

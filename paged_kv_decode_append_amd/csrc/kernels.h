@@ -50,12 +50,48 @@ inline int32_t append_groups(int64_t rows) {
   return rows <= 0 ? 0 : (int32_t)std::min<int64_t>((rows + 7) / 8, 128);
 }
 
+// A decode launch's merge of its split attention left for the step's
+// combined merge (launch_prefill with `fold`): the partition grid's partials
+// (one work-group per (sequence, query head)) or the balanced schedule's
+// pieces (one per (unit, query head)).
+struct DecodeMerge {
+  int32_t groups = 0;  // work-groups of the merge (0: none left)
+  bool pieces = false;
+  const float* part_o = nullptr;
+  const float* part_ml = nullptr;
+  // partition grid
+  const int32_t* context_lens = nullptr;
+  int32_t ctx_clamp = 0, partition_blocks = 0, max_parts = 0, num_q_heads = 0;
+  // schedule pieces
+  const int32_t* sched = nullptr;
+  int32_t units = 0, sched_groups = 0, num_kv_heads = 0, group = 0;
+};
+
+// The merge of the partition grid's partials, as launch_decode_merge runs it.
+inline DecodeMerge grid_merge(const float* part_o, const float* part_ml,
+                              const int32_t* context_lens, int32_t ctx_clamp,
+                              const DecodePlan& plan, int32_t num_decode_seqs,
+                              int32_t num_q_heads) {
+  DecodeMerge m;
+  m.groups = num_decode_seqs * num_q_heads;
+  m.part_o = part_o;
+  m.part_ml = part_ml;
+  m.context_lens = context_lens;
+  m.ctx_clamp = ctx_clamp;
+  m.partition_blocks = plan.partition_blocks;
+  m.max_parts = plan.max_parts;
+  m.num_q_heads = num_q_heads;
+  return m;
+}
+
+// With `defer` set, a merge the launch needs is described there instead of
+// launched (the decode launchers below).
 hipError_t launch_paged_decode(const void* q, void* k_pool, void* v_pool, int64_t num_blocks,
                                int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t num_decode_seqs, float scale,
                                const DecodePlan& plan, const DecodeAppend& app, void* out,
-                               void* workspace, hipStream_t stream);
+                               void* workspace, hipStream_t stream, DecodeMerge* defer = nullptr);
 
 // Log-sum-exp merge of the split-KV partitions written by a decode kernel
 // (partials [rows][max_parts] of (o / l) and (m, l)); rows with a single
@@ -82,7 +118,8 @@ hipError_t launch_paged_decode_fp8(const void* q, void* k_codes, void* v_codes, 
                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                                    const int32_t* context_lens, int32_t num_decode_seqs,
                                    float scale, const DecodePlan& plan, const DecodeAppend& app,
-                                   void* out, void* workspace, hipStream_t stream);
+                                   void* out, void* workspace, hipStream_t stream,
+                                   DecodeMerge* defer = nullptr);
 
 // Balanced decode schedule (decode_sched.hip): made once per step on the
 // device from the context lengths, read by every layer's decode launch.
@@ -108,7 +145,8 @@ hipError_t launch_paged_decode_scheduled(const void* q, void* k_pool, void* v_po
                                          int32_t max_blocks_per_seq, int32_t num_decode_seqs,
                                          float scale, const DecodeSchedulePlan& plan,
                                          const void* schedule, const DecodeAppend& app,
-                                         void* out, void* workspace, hipStream_t stream);
+                                         void* out, void* workspace, hipStream_t stream,
+                                         DecodeMerge* defer = nullptr);
 
 // Split-KV plan of the prefill chunks: each 64-row query tile is cut into
 // `splits` ranges of context tiles, merged by log-sum-exp when splits > 1.
@@ -139,6 +177,10 @@ hipError_t launch_prefill_wide(const void* q, const void* k_pool, const void* v_
 // Causal attention of the prefill chunks (sequences first_seq ..
 // first_seq + num_prefill_seqs - 1) on the matrix cores.  With k_scale set
 // the pools hold fp8 (E4M3) codes and k_scale / v_scale their row scales.
+// With `fold` holding a decode merge left by the decode launch, that merge
+// runs in the same launch as the chunks' merge (or alone, when the chunks
+// need none), after the prefill kernel; the decode partials must then lie
+// outside `workspace`.
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           const float* k_scale, const float* v_scale, int64_t num_blocks,
                           int32_t num_kv_heads, int32_t num_q_heads, int32_t head_dim,
@@ -146,6 +188,6 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* context_lens, const int32_t* query_start_loc,
                           int32_t first_seq, int32_t num_prefill_seqs, int32_t max_query_len,
                           float scale, const PrefillPlan& plan, void* out, void* workspace,
-                          hipStream_t stream);
+                          hipStream_t stream, const DecodeMerge* fold = nullptr);
 
 }  // namespace pkv

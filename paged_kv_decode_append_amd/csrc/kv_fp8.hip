@@ -640,7 +640,7 @@ hipError_t launch_decode_fp8_dg(const void* q, void* k_codes, void* v_codes, flo
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
                                 int32_t num_decode_seqs, float scale, const DecodePlan& plan,
                                 const DecodeAppend& app, void* out, void* workspace,
-                                hipStream_t stream) {
+                                hipStream_t stream, DecodeMerge* defer) {
   const int32_t num_q_heads = num_kv_heads * G;
   const int64_t clamp64 = std::min<int64_t>((int64_t)max_blocks_per_seq * 16,
                                             (int64_t)plan.max_parts * plan.partition_blocks * 16);
@@ -666,6 +666,11 @@ hipError_t launch_decode_fp8_dg(const void* q, void* k_codes, void* v_codes, flo
                      app.num_tokens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.max_parts <= 1) return err;
+  if (defer) {
+    *defer = grid_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
+                        num_q_heads);
+    return hipSuccess;
+  }
   return launch_decode_merge(part_o, part_ml, context_lens, ctx_clamp, plan, num_decode_seqs,
                              num_q_heads, D, out, stream);
 }
@@ -676,16 +681,18 @@ hipError_t launch_decode_fp8_d(int32_t group, const void* q, void* kc, void* vc,
                                const int32_t* bt, int32_t maxblk, const int32_t* ctx,
                                int32_t nseq, float scale, const DecodePlan& plan,
                                const DecodeAppend& app, void* out, void* ws,
-                               hipStream_t stream) {
+                               hipStream_t stream, DecodeMerge* defer) {
   const bool fused = app.k_new != nullptr;
 #define PKV_CASE(GG)                                                                          \
   case GG:                                                                                   \
     return fused ? launch_decode_fp8_dg<D, GG, true>(q, kc, vc, ks, vs, num_blocks,          \
                                                      num_kv_heads, bt, maxblk, ctx, nseq,    \
-                                                     scale, plan, app, out, ws, stream)      \
+                                                     scale, plan, app, out, ws, stream,      \
+                                                     defer)                                  \
                  : launch_decode_fp8_dg<D, GG, false>(q, kc, vc, ks, vs, num_blocks,         \
                                                       num_kv_heads, bt, maxblk, ctx, nseq,   \
-                                                      scale, plan, app, out, ws, stream);
+                                                      scale, plan, app, out, ws, stream,     \
+                                                      defer);
   switch (group) {
     PKV_CASE(1) PKV_CASE(2) PKV_CASE(3) PKV_CASE(4)
     PKV_CASE(5) PKV_CASE(6) PKV_CASE(7) PKV_CASE(8)
@@ -726,19 +733,20 @@ hipError_t launch_paged_decode_fp8(const void* q, void* k_codes, void* v_codes, 
                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
                                    const int32_t* context_lens, int32_t num_decode_seqs,
                                    float scale, const DecodePlan& plan, const DecodeAppend& app,
-                                   void* out, void* workspace, hipStream_t stream) {
+                                   void* out, void* workspace, hipStream_t stream,
+                                   DecodeMerge* defer) {
   if (num_decode_seqs == 0) return hipSuccess;
   const int32_t group = num_q_heads / num_kv_heads;
   if (head_dim == 128)
     return launch_decode_fp8_d<128>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
                                     num_kv_heads, block_tables, max_blocks_per_seq,
                                     context_lens, num_decode_seqs, scale, plan, app, out,
-                                    workspace, stream);
+                                    workspace, stream, defer);
   if (head_dim == 256)
     return launch_decode_fp8_d<256>(group, q, k_codes, v_codes, k_scale, v_scale, num_blocks,
                                     num_kv_heads, block_tables, max_blocks_per_seq,
                                     context_lens, num_decode_seqs, scale, plan, app, out,
-                                    workspace, stream);
+                                    workspace, stream, defer);
   return hipErrorInvalidValue;
 }
 

@@ -40,6 +40,7 @@
 #include "device_util.h"
 #include "fp8_util.h"
 #include "kernels.h"
+#include "merge.h"
 
 namespace pkv {
 
@@ -54,7 +55,7 @@ constexpr int64_t kCUs = 256;
 constexpr int64_t kGroupsPerCU128 = 3;
 constexpr int64_t kGroupsPerCU256 = 2;
 constexpr uint32_t kXcds = 8;
-constexpr int64_t kMaxPrefillSplits = 16;
+using merge::kMaxPrefillSplits;
 constexpr int64_t kPackedRounds = 2;  // packed rows: target rounds of resident work-groups
 // long-chunk kernels at d = 128 (fp16 and fp8 caches): 256 rows per
 // work-group, one per CU, counted in 128-row groups, two per CU
@@ -514,61 +515,39 @@ __global__ __launch_bounds__(256, HPW == 1 ? (D == 128 ? kGroupsPerCU128 : kGrou
 }
 
 // Merge of the splits of every (prefill row, query head): one wave each.
-//   M = max m_s over splits with l_s > 0, w_s = l_s 2^(m_s - M),
-//   O = sum_s w_s o_s / sum_s w_s.
-// Lane s holds split s's (m, l), so the weights take one round of loads and
-// two wave reductions; every split's o is then requested at once (a split
-// that saw no position -- l = 0 -- may have left o unwritten: its value is
-// read but selected away, never multiplied).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ query_start_loc, int32_t first_seq, int32_t num_seqs,
     int32_t num_q_heads, int32_t num_splits, int64_t max_row_heads, uint16_t* __restrict__ out) {
-  constexpr int EPL = D / 64;
-  static_assert(kMaxPrefillSplits <= 64, "one lane per split");
-  const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t first_row = query_start_loc[first_seq];
-  const int64_t rows = (int64_t)query_start_loc[num_seqs] - first_row;
-  if (rh >= rows * num_q_heads || rh >= max_row_heads) return;
-  const float* ml = part_ml + rh * num_splits * 2;
-  float m = -__builtin_huge_valf(), l = 0.f;
-  if (lane < num_splits) {
-    m = ml[2 * lane];
-    l = ml[2 * lane + 1];
+  merge::chunk_merge_row_head<D>(part_o, part_ml, query_start_loc, first_seq, num_seqs,
+                                 num_q_heads, num_splits, max_row_heads, out,
+                                 (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// The step's combined merge: the decode part's merge left by its launch (work-
+// groups 0 .. dm.groups - 1: partition grid rows or schedule pieces) and the
+// chunks' merge (the rest, four (row, head) pairs each) in one launch after
+// the prefill kernel.  They write different rows of `out`.
+template <int D>
+__global__ __launch_bounds__(256) void step_merge_kernel(
+    DecodeMerge dm, const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ query_start_loc, int32_t first_seq, int32_t num_seqs,
+    int32_t num_q_heads, int32_t num_splits, int64_t max_row_heads, uint16_t* __restrict__ out) {
+  const int64_t w = blockIdx.x;
+  if (w < dm.groups) {  // uniform over the work-group
+    if (dm.pieces)
+      merge::piece_merge_unit<D>(dm.sched, dm.units, dm.sched_groups, dm.num_kv_heads, dm.group,
+                                 dm.part_o, dm.part_ml, out, (int32_t)(w / dm.group),
+                                 (int32_t)(w % dm.group));
+    else
+      merge::lse_merge_row<D>(dm.part_o, dm.part_ml, dm.context_lens, dm.ctx_clamp,
+                              dm.partition_blocks, dm.max_parts, dm.num_q_heads, out, (int)w);
+    return;
   }
-  // Every split's o is requested before the weights are known (one memory
-  // round trip, not two); loads of splits past num_splits re-read the last
-  // one (in bounds) and get weight 0.
-  const float* src = part_o + rh * num_splits * D + EPL * lane;
-  float o[kMaxPrefillSplits][EPL];
-#pragma unroll
-  for (int s = 0; s < kMaxPrefillSplits; ++s) {
-    const int sc = min(s, num_splits - 1);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[s][e] = src[(int64_t)sc * D + e];
-  }
-  float M = l > 0.f ? m : -__builtin_huge_valf();
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  const float w = l > 0.f ? l * fast_exp2(m - M) : 0.f;
-  float W = w;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
-  float acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxPrefillSplits; ++s) {
-    const float ws = s < num_splits ? __shfl(w, s) : 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += ws > 0.f ? ws * o[s][e] : 0.f;
-  }
-  uint16_t* dst = out + (first_row * num_q_heads + rh) * D + EPL * lane;
-  const float inv = W > 0.f ? 1.f / W : 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = __builtin_bit_cast(uint16_t, (f16)(acc[e] * inv));
+  merge::chunk_merge_row_head<D>(part_o, part_ml, query_start_loc, first_seq, num_seqs,
+                                 num_q_heads, num_splits, max_row_heads, out,
+                                 (w - dm.groups) * 4 + (threadIdx.x >> 6));
 }
 
 }  // namespace
@@ -622,6 +601,31 @@ PrefillPlan plan_prefill(int32_t num_prefill_seqs, int32_t num_q_heads, int32_t 
   return plan;
 }
 
+// The chunks' merge (when split), with the decode part's merge folded in when
+// its launch left one.
+template <int D>
+static hipError_t launch_chunk_merges(const PrefillPlan& plan, const float* part_o,
+                                      const float* part_ml, const int32_t* query_start_loc,
+                                      int32_t first_seq, int32_t num_prefill_seqs,
+                                      int32_t num_q_heads, void* out, const DecodeMerge* fold,
+                                      hipStream_t stream) {
+  const int64_t chunk_groups = plan.splits > 1 ? (plan.max_row_heads + 3) / 4 : 0;
+  const int64_t dec_groups = fold ? fold->groups : 0;
+  if (chunk_groups + dec_groups == 0) return hipSuccess;
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls
+  if (dec_groups == 0)
+    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)chunk_groups), dim3(256), 0,
+                       stream, part_o, part_ml, query_start_loc, first_seq,
+                       first_seq + num_prefill_seqs, num_q_heads, plan.splits,
+                       plan.max_row_heads, static_cast<uint16_t*>(out));
+  else
+    hipLaunchKernelGGL(step_merge_kernel<D>, dim3((uint32_t)(dec_groups + chunk_groups)),
+                       dim3(256), 0, stream, *fold, part_o, part_ml, query_start_loc, first_seq,
+                       first_seq + num_prefill_seqs, num_q_heads, plan.splits,
+                       plan.max_row_heads, static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
 template <int D, bool FP8>
 static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void* v_pool,
                                    const float* k_scale, const float* v_scale, int64_t num_blocks, int32_t num_kv_heads, int32_t num_q_heads,
@@ -629,7 +633,8 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                                    const int32_t* context_lens, const int32_t* query_start_loc,
                                    int32_t first_seq, int32_t num_prefill_seqs,
                                    int32_t max_query_len, float scale, const PrefillPlan& plan,
-                                   void* out, void* workspace, hipStream_t stream) {
+                                   void* out, void* workspace, hipStream_t stream,
+                                   const DecodeMerge* fold) {
   const int32_t ctx_clamp =
       (int32_t)std::min<int64_t>((int64_t)max_blocks_per_seq * 16, INT32_MAX);
   float* part_o = static_cast<float*>(workspace);
@@ -640,13 +645,9 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                               num_q_heads, block_tables, max_blocks_per_seq, context_lens,
                               query_start_loc, first_seq, num_prefill_seqs, max_query_len, scale,
                               plan.splits, out, part_o, part_ml, stream);
-    if (err != hipSuccess || plan.splits == 1) return err;
-    const int64_t waves = plan.max_row_heads;
-    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0,
-                       stream, part_o, part_ml, query_start_loc, first_seq,
-                       first_seq + num_prefill_seqs, num_q_heads, plan.splits,
-                       plan.max_row_heads, static_cast<uint16_t*>(out));
-    return hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_chunk_merges<D>(plan, part_o, part_ml, query_start_loc, first_seq,
+                                  num_prefill_seqs, num_q_heads, out, fold, stream);
   }
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   if (plan.packed) {
@@ -675,13 +676,9 @@ static hipError_t launch_prefill_d(const void* q, const void* k_pool, const void
                        static_cast<uint16_t*>(out), part_o, part_ml);
   }
   err = hipGetLastError();
-  if (err != hipSuccess || plan.splits == 1) return err;
-  const int64_t waves = plan.max_row_heads;
-  hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0,
-                     stream, part_o, part_ml, query_start_loc, first_seq,
-                     first_seq + num_prefill_seqs, num_q_heads, plan.splits, plan.max_row_heads,
-                     static_cast<uint16_t*>(out));
-  return hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_chunk_merges<D>(plan, part_o, part_ml, query_start_loc, first_seq,
+                                num_prefill_seqs, num_q_heads, out, fold, stream);
 }
 
 hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
@@ -691,13 +688,13 @@ hipError_t launch_prefill(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* context_lens, const int32_t* query_start_loc,
                           int32_t first_seq, int32_t num_prefill_seqs, int32_t max_query_len,
                           float scale, const PrefillPlan& plan, void* out, void* workspace,
-                          hipStream_t stream) {
+                          hipStream_t stream, const DecodeMerge* fold) {
   if (num_prefill_seqs <= 0) return hipSuccess;
   const bool fp8 = k_scale != nullptr;
 #define PKV_PREFILL_ARGS                                                                      \
   q, k_pool, v_pool, k_scale, v_scale, num_blocks, num_kv_heads, num_q_heads, block_tables,  \
       max_blocks_per_seq, context_lens, query_start_loc, first_seq, num_prefill_seqs,         \
-      max_query_len, scale, plan, out, workspace, stream
+      max_query_len, scale, plan, out, workspace, stream, fold
   if (head_dim == 128)
     return fp8 ? launch_prefill_d<128, true>(PKV_PREFILL_ARGS)
                : launch_prefill_d<128, false>(PKV_PREFILL_ARGS);
