@@ -34,15 +34,16 @@ struct DecodePlan {
 DecodePlan plan_decode(int32_t num_decode_seqs, int32_t num_kv_heads, int32_t num_q_heads,
                        int32_t head_dim, int32_t max_context_len, int32_t kv_partition_tokens);
 
-// The decode tokens' rows to append inside the decode kernel (row i of
-// k_new / v_new [num_decode_seqs][Hkv][d] to slot_mapping[i]); all null for
-// attention only.
+// The step's new rows to append inside the decode launch: row t of k_new /
+// v_new [num_tokens][Hkv][d] goes to slot_mapping[t]; the decode rows
+// (t < num_decode_seqs) by the work-group that attends that position, the
+// prefill chunks' rows after them by extra work-groups.  All null (and
+// num_tokens 0) for attention only.
 struct DecodeAppend {
   const void* k_new;
   const void* v_new;
   const int64_t* slot_mapping;
-  int32_t num_tokens;  // rows of k_new / v_new: rows past the decode rows (prefill
-                       // chunks' tokens) are appended by extra work-groups
+  int32_t num_tokens;
 };
 
 // Work-groups a decode launch adds for appending `rows` prefill rows.
