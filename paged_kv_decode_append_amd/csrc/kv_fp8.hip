@@ -57,6 +57,12 @@ constexpr int kBlockSize = 16;
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // lazy max (base 2)
+// Unused dynamic LDS of a d = 128 decode work-group: with it a work-group
+// holds more than a third of the CU's 160 KiB, so at most two are resident
+// per CU (two waves per SIMD) whatever the register count.  Measured: at
+// three per CU the ragged grid's work-groups pack onto fewer CUs and the
+// ragged batch slows by ~15%.
+constexpr size_t kResidencyPadBytes = 40 << 10;
 
 // Smallest e with amax <= 448 x 2^e (0 for amax = 0).  amax is a finite fp16
 // value, a normal fp32 number: amax = 1.f x 2^k; 448 = 1.75 x 2^8, so
@@ -302,12 +308,9 @@ __device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs
     vsv[i] = valid ? vs[i] : 0.f;
     vmax = fmaxf(vmax, vsv[i]);
   }
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
-  vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+  vmax = max_of_rows(vmax);  // over the four lane groups' tokens
   if (__any(grow)) {
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float bm = max_of_rows(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
     const float mn = fmaxf(st.m, bm);
     const float alpha = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
     st.l *= alpha;
@@ -322,7 +325,10 @@ __device__ __forceinline__ float block_scores8(KV8Regs<D>& r, const uint16_t* qs
 #pragma unroll
       for (int i = 0; i < 4; ++i) st.acc[ct][i] *= a[i];
   }
-  const float inv_vmax = vmax > 0.f ? 1.f / vmax : 0.f;  // a power of two: exact
+  // vmax is a power of two (or 0): 1 / vmax = 2 x 2^-k for vmax = 0.5 x 2^k,
+  // exact, without a division
+  const float inv_vmax =
+      vmax > 0.f ? __builtin_ldexpf(2.f, -__builtin_amdgcn_frexp_expf(vmax)) : 0.f;
   const float neg_m = st.m == kNegInf ? 0.f : -st.m;
   float p[4];
 #pragma unroll
@@ -655,7 +661,8 @@ hipError_t launch_decode_fp8_dg(const void* q, void* k_codes, void* v_codes, flo
       APPEND ? (int32_t)((append_groups(app.num_tokens - num_decode_seqs) + xy - 1) / xy) : 0;
   (void)hipGetLastError();  // drop errors left by earlier runtime calls
   hipLaunchKernelGGL((paged_decode_fp8_kernel<D, G, APPEND>),
-                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts + app_z), dim3(64 * kWaves), 0,
+                     dim3(num_decode_seqs, num_kv_heads, plan.max_parts + app_z), dim3(64 * kWaves),
+                     D == 128 ? kResidencyPadBytes : 0,
                      stream, static_cast<const uint16_t*>(q), static_cast<uint8_t*>(k_codes),
                      static_cast<uint8_t*>(v_codes), k_scale, v_scale, num_blocks,
                      num_kv_heads, block_tables, max_blocks_per_seq, context_lens, ctx_clamp,
