@@ -83,3 +83,51 @@ def test_largest_query_group_with_one_kv_head(d):
     wl = workloads.custom("g8", ctx, new, 5, 8, 1, d, seed=83 + d)
     _, _, errs = run_layer_and_check(wl)
     print(f"[parity] G=8 Hkv=1 d={d}: max_abs={errs[0]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("kv,use_schedule", [("fp16", False), ("fp16", True), ("fp8", False)])
+def test_mixed_step_with_padded_prefill_rows(kv, use_schedule):
+    """A fused step of decodes and chunks where every third prefill row has
+    slot -1: the decode launch's extra work-groups write the other prefill
+    rows and skip those, whose positions keep the pool's row, which the
+    chunk then attends (pools bit-exact against the oracle's append replay)."""
+    from paged_kv_decode_append_amd.step import Step
+
+    ctx = [300, 40, 1025, 700, 130]
+    new = [1, 1, 1, 200, 65]
+    wl = workloads.custom("pad_chunks", ctx, new, 3, 12, 2, 128, seed=83)
+    step = Step.from_workload(wl, use_schedule=use_schedule)
+    step.plan()
+    slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, wl.query_start_loc, 16)
+    slots[3::3] = -1                       # prefill rows 3, 6, 9, ... (decode rows are 0..2)
+    slots_t = torch.from_numpy(slots).cuda()
+    if kv == "fp16":
+        t = workloads.layer_tensors(wl, 0, device="cuda")
+        cache = pkv.KVCache(t["k_pool"], t["v_pool"])
+        before = [host_bits(t["k_pool"]), host_bits(t["v_pool"])]
+    else:
+        t = workloads.layer_tensors_fp8(wl, 0, device="cuda")
+        cache = pkv.KVCache(t["k_codes"], t["v_codes"], t["k_scale"], t["v_scale"])
+        before = [t[k].cpu().numpy() for k in ("k_codes", "v_codes", "k_scale", "v_scale")]
+    out = torch.full_like(t["q"], float("nan"))
+    pkv.append_attention_step(cache, t["k_new"], t["v_new"], slots_t, t["q"], out,
+                              step.block_tables, step.context_lens, step.query_start_loc,
+                              wl.num_decode_seqs, wl.scale, step.max_context_len,
+                              step.max_query_len, workspace=step.workspace,
+                              schedule=step.schedule)
+    torch.cuda.synchronize()
+    kn, vn, q = host_bits(t["k_new"]), host_bits(t["v_new"]), host_bits(t["q"])
+    if kv == "fp16":
+        kref, vref = oracle.kv_append(before[0], before[1], kn, vn, slots)
+        assert np.array_equal(host_bits(t["k_pool"]), kref)
+        assert np.array_equal(host_bits(t["v_pool"]), vref)
+        ref = oracle.paged_attention(q, kref, vref, wl.block_tables, wl.context_lens,
+                                     wl.query_start_loc, wl.scale)
+    else:
+        from oracle import fp8 as ofp8
+        after = ofp8.kv_append(*before, kn, vn, slots)
+        for name, want in zip(("k_codes", "v_codes", "k_scale", "v_scale"), after):
+            assert np.array_equal(t[name].cpu().numpy(), want), name
+        ref = oracle.paged_attention_fp8(q, *after, wl.block_tables, wl.context_lens,
+                                         wl.query_start_loc, wl.scale)
+    assert_close(out.cpu().numpy(), ref, f"padded prefill rows {kv} schedule={use_schedule}")
