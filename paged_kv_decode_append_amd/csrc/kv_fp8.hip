@@ -57,12 +57,12 @@ constexpr int kBlockSize = 16;
 constexpr int kWaves = 4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.f;  // lazy max (base 2)
-// Unused dynamic LDS of a d = 128 decode work-group: with it a work-group
-// holds more than a third of the CU's 160 KiB, so at most two are resident
-// per CU (two waves per SIMD) whatever the register count.  Measured: at
-// three per CU the ragged grid's work-groups pack onto fewer CUs and the
-// ragged batch slows by ~15%.
-constexpr size_t kResidencyPadBytes = 40 << 10;
+// Unused dynamic LDS of a d = 128 decode work-group: by itself more than a
+// third of the CU's 160 KiB (whatever the group size G makes the static
+// part), so at most two work-groups are resident per CU (two waves per
+// SIMD) whatever the register count.  Measured: at three per CU the ragged
+// grid's work-groups pack onto fewer CUs and the ragged batch slows by ~15%.
+constexpr size_t kResidencyPadBytes = 54 << 10;
 
 // Smallest e with amax <= 448 x 2^e (0 for amax = 0).  amax is a finite fp16
 // value, a normal fp32 number: amax = 1.f x 2^k; 448 = 1.75 x 2^8, so
