@@ -56,7 +56,10 @@
 extern "C" {
 #endif
 
-#define PKV_VERSION 1
+/* ABI version.  2: a mixed step's workspace holds the chunks' partials after
+ * the decode part's (pkv_attention_step_workspace grew accordingly), and
+ * pkv_validate_step reports code 10. */
+#define PKV_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
