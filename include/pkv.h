@@ -57,7 +57,7 @@ extern "C" {
 #endif
 
 /* ABI version.  2: a mixed step's workspace holds the chunks' partials after
- * the decode part's (pkv_attention_step_workspace grew accordingly), and
+ * the decode part's (pkv_attention_workspace_size grew accordingly), and
  * pkv_validate_step reports code 10. */
 #define PKV_VERSION 2
 
