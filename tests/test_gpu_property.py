@@ -2,7 +2,8 @@
 oracle.  Each example draws head size, KV heads and query group, a mix of
 single-token decodes and causal chunks (1..160 rows, some covering the whole
 context, others after a cached prefix) with ragged contexts, the split-KV
-partition length, fused or separate append, and an fp16 or fp8 cache.
+partition length, fused or separate append, an fp16 or fp8 cache, and the
+balanced decode schedule left to the step, forced on or forced off.
 Checks, as the fixed-case tests do: slot mapping and pools bit-exact after
 the append, every query row within the attention tolerance.
 
@@ -12,7 +13,7 @@ prints its case before it runs."""
 import numpy as np
 import pytest
 import torch
-from hypothesis import HealthCheck, Phase, given, settings, strategies as st
+from hypothesis import HealthCheck, Phase, example, given, settings, strategies as st
 
 import oracle
 import paged_kv_decode_append_amd as pkv
@@ -47,7 +48,10 @@ def steps(draw):
     fused = draw(st.booleans())
     fp8 = draw(st.booleans())
     seed = draw(st.integers(0, 2**20))
-    return d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed
+    # balanced decode schedule: the step's default, forced on or forced off
+    # (an fp16 cache at d = 128 only; elsewhere the partition grid runs anyway)
+    sched = draw(st.sampled_from([None, True, False]))
+    return d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed, sched
 
 
 def _fp8_step(wl, part, fused):
@@ -88,14 +92,22 @@ def _fp8_step(wl, part, fused):
           phases=(Phase.explicit, Phase.generate), print_blob=True,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(steps())
+# the derandomized draws reach the balanced schedule's choices rarely: these
+# take it on a pure-decode step (fused and separate append), leave it to a
+# mixed step, and keep it off one
+@example((128, 2, 6, [1500, 37, 900, 3000, 260, 1], [1] * 6, 6, 0, True, False, 11, True))
+@example((128, 2, 6, [1500, 37, 900, 3000, 260, 1], [1] * 6, 6, 0, False, False, 11, True))
+@example((128, 1, 8, [2500, 700, 90, 600], [1, 1, 1, 40], 3, 0, True, False, 13, None))
+@example((128, 4, 4, [3000, 200, 1200, 160], [1, 1, 1, 160], 3, 0, True, False, 12, False))
 def test_random_steps_match_the_oracle(case):
-    d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed = case
+    d, hkv, g, ctx, new, n_dec, part, fused, fp8, seed, sched = case
     name = (f"d={d} Hkv={hkv} G={g} ctx={ctx} new={new} decodes={n_dec} part={part} "
-            f"fused={fused} fp8={fp8} seed={seed}")
+            f"fused={fused} fp8={fp8} seed={seed} schedule={sched}")
     print(f"[property] {name}", flush=True)
     wl = workloads.custom("property", ctx, new, n_dec, hkv * g, hkv, d, seed=seed)
     if fp8:
         errs = _fp8_step(wl, part, fused)
     else:
-        _, _, errs = run_layer_and_check(wl, kv_partition_tokens=part, fused=fused)
+        _, _, errs = run_layer_and_check(wl, kv_partition_tokens=part, fused=fused,
+                                         use_schedule=sched)
     print(f"[property]   max_abs={errs[0]:.2e} norm_rel={errs[1]:.2e}", flush=True)
