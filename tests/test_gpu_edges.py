@@ -85,21 +85,33 @@ def test_largest_query_group_with_one_kv_head(d):
     print(f"[parity] G=8 Hkv=1 d={d}: max_abs={errs[0]:.2e}", flush=True)
 
 
-@pytest.mark.parametrize("kv,use_schedule", [("fp16", False), ("fp16", True), ("fp8", False)])
-def test_mixed_step_with_padded_prefill_rows(kv, use_schedule):
+# (context lengths, new tokens, decodes, query heads, KV heads, head size):
+# short chunks, and one chunk longer than the decode launch's extra
+# work-groups take in one row each (more than 128 x 8 rows)
+PADDED_STEPS = {
+    "short": ([300, 40, 1025, 700, 130], [1, 1, 1, 200, 65], 3, 12, 2),
+    "long": ([900, 75, 1700], [1, 1, 1500], 2, 4, 1),
+}
+
+
+@pytest.mark.parametrize("kv,use_schedule,d,shape", [
+    ("fp16", False, 128, "short"), ("fp16", True, 128, "short"), ("fp8", False, 128, "short"),
+    ("fp16", False, 256, "short"), ("fp8", False, 256, "short"),
+    ("fp16", False, 128, "long"), ("fp16", True, 128, "long"), ("fp8", False, 256, "long")])
+def test_mixed_step_with_padded_prefill_rows(kv, use_schedule, d, shape):
     """A fused step of decodes and chunks where every third prefill row has
     slot -1: the decode launch's extra work-groups write the other prefill
     rows and skip those, whose positions keep the pool's row, which the
     chunk then attends (pools bit-exact against the oracle's append replay)."""
     from paged_kv_decode_append_amd.step import Step
 
-    ctx = [300, 40, 1025, 700, 130]
-    new = [1, 1, 1, 200, 65]
-    wl = workloads.custom("pad_chunks", ctx, new, 3, 12, 2, 128, seed=83)
+    ctx, new, n_dec, hq, hkv = PADDED_STEPS[shape]
+    print(f"[parity] padded prefill rows {shape} {kv} d={d} schedule={use_schedule}", flush=True)
+    wl = workloads.custom("pad_chunks", ctx, new, n_dec, hq, hkv, d, seed=83)
     step = Step.from_workload(wl, use_schedule=use_schedule)
     step.plan()
     slots = oracle.slot_mapping(wl.block_tables, wl.context_lens, wl.query_start_loc, 16)
-    slots[3::3] = -1                       # prefill rows 3, 6, 9, ... (decode rows are 0..2)
+    slots[n_dec::3] = -1                   # every third prefill row (decode rows come first)
     slots_t = torch.from_numpy(slots).cuda()
     if kv == "fp16":
         t = workloads.layer_tensors(wl, 0, device="cuda")
@@ -130,4 +142,5 @@ def test_mixed_step_with_padded_prefill_rows(kv, use_schedule):
             assert np.array_equal(t[name].cpu().numpy(), want), name
         ref = oracle.paged_attention_fp8(q, *after, wl.block_tables, wl.context_lens,
                                          wl.query_start_loc, wl.scale)
-    assert_close(out.cpu().numpy(), ref, f"padded prefill rows {kv} schedule={use_schedule}")
+    assert_close(out.cpu().numpy(), ref, f"padded prefill rows {shape} {kv} d={d} "
+                 f"schedule={use_schedule}")
